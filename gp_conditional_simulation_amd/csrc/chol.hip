@@ -1,0 +1,369 @@
+// Adaptive mixed-precision tile Cholesky on one MI355X.
+//
+// "Mixed-Precision GPU Acceleration for Confidence Regions of Spatial Excursion Sets",
+// Sec. IV-B and Algorithm 2 (step 12): the scaled covariance s^2 V, cut into nb x nb tiles with a
+// per-tile precision map, is factored right-looking.  Step k:
+//   * diagonal tile (k, k): FP64 POTRF.  Here it is factored together with its explicit inverse
+//     T_k = L_kk^-1 by recursive halving down to a single-workgroup 64 x 64 leaf (LDS resident);
+//     the halves are joined with FP64 matrix-core GEMMs.
+//   * panel tiles (i, k), i > k: L_ik = A_ik L_kk^-T evaluated as the product A_ik T_k^T in the
+//     tile's precision (FP64 tiles in FP64, FP32 and FP16 tiles in FP32 with FP16 stored back),
+//     one batched launch per compute precision.
+//   * trailing tiles (i, j), k < j <= i: A_ij -= L_ik L_jk^T in the precision of A_ij with the
+//     operands converted to it (FP16 on FP16 matrix cores with FP32 accumulation), one batched
+//     launch per compute precision; diagonal tiles (the SYRK tasks) are FP64.
+// The T_k are kept in the handle: kriging reuses them for its blocked triangular solves.
+#include <algorithm>
+#include <cmath>
+
+#include "common.h"
+#include "devutil.h"
+
+namespace gpex {
+
+// ---------------------------------------------------------------------------------------------
+__global__ void k_copy2d(const void* src, int tsrc, int64_t lds, void* dst, int tdst, int64_t ldd,
+                         int64_t rows, int64_t cols, double scale, unsigned long long* flags) {
+    int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int64_t c = blockIdx.y;
+    bool ovf = false;
+    for (; c < cols; c += gridDim.y) {
+        if (r < rows) {
+            double v = load_as_double(src, tsrc, r + c * lds);
+            if (scale != 1.0) v *= scale;
+            ovf |= store_from_double(dst, tdst, r + c * ldd, v);
+        }
+    }
+    if (ovf && flags) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
+}
+
+int copy2d(gpex_ctx_t ctx, hipStream_t s, const void* src, int tsrc, int64_t lds, void* dst,
+           int tdst, int64_t ldd, int64_t rows, int64_t cols, double scale) {
+    if (rows <= 0 || cols <= 0) return GPEX_OK;
+    dim3 grid((unsigned)((rows + 255) / 256), (unsigned)std::min<int64_t>(cols, 65535));
+    hipLaunchKernelGGL(k_copy2d, grid, dim3(256), 0, s, src, tsrc, lds, dst, tdst, ldd, rows, cols,
+                       scale, reinterpret_cast<unsigned long long*>(ctx->d_flags));
+    GPEX_HIP(ctx, hipGetLastError());
+    return GPEX_OK;
+}
+
+__global__ void k_zero2d(double* dst, int64_t ldd, int64_t rows, int64_t cols) {
+    int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t c = blockIdx.y; c < cols; c += gridDim.y)
+        if (r < rows) dst[r + c * ldd] = 0.0;
+}
+
+int zero2d(gpex_ctx_t ctx, hipStream_t s, double* dst, int64_t ldd, int64_t rows, int64_t cols) {
+    if (rows <= 0 || cols <= 0) return GPEX_OK;
+    dim3 grid((unsigned)((rows + 255) / 256), (unsigned)std::min<int64_t>(cols, 65535));
+    hipLaunchKernelGGL(k_zero2d, grid, dim3(256), 0, s, dst, ldd, rows, cols);
+    GPEX_HIP(ctx, hipGetLastError());
+    return GPEX_OK;
+}
+
+// Batched raw byte copy: task q copies bytes[q] bytes (a multiple of 16) from src[q] to dst[q].
+struct CopyTask {
+    const void* src;
+    void* dst;
+    int64_t bytes;
+};
+
+__global__ void k_copy_tasks(const CopyTask* tasks, int64_t chunk) {
+    const CopyTask& T = tasks[blockIdx.y];
+    int64_t beg = (int64_t)blockIdx.x * chunk;
+    int64_t end = beg + chunk < T.bytes ? beg + chunk : T.bytes;
+    const uint4* s = static_cast<const uint4*>(T.src);
+    uint4* d = static_cast<uint4*>(T.dst);
+    for (int64_t i = beg / 16 + threadIdx.x; i < end / 16; i += blockDim.x) d[i] = s[i];
+}
+
+// ---------------------------------------------------------------------------------------------
+// Leaf: factor an n x n (n <= 64) FP64 block in LDS and invert its factor.
+//   Cholesky: right-looking over columns, three barriers per column.
+//   Inverse: thread j computes column j of L^-1 by forward substitution.
+// Writes L (upper part zeroed) back to A and L^-1 (upper zeroed) to T.  A non-positive pivot at
+// local column k records col0 + k + 1 in flags[FLAG_INFO] unless an earlier failure is recorded.
+constexpr int LEAF = 64;
+
+__global__ __launch_bounds__(256) void k_potrf_leaf(double* A, int64_t lda, double* T, int64_t ldt,
+                                                    int n, int64_t col0, unsigned long long* flags) {
+    __shared__ double s[LEAF][LEAF + 1];
+    __shared__ double x[LEAF][LEAF + 1];
+    const int tid = threadIdx.x;
+    for (int idx = tid; idx < n * n; idx += 256) {
+        int i = idx % n, j = idx / n;
+        s[i][j] = (i >= j) ? A[i + (int64_t)j * lda] : 0.0;
+    }
+    __syncthreads();
+    int bad = 0;
+    for (int k = 0; k < n; ++k) {
+        double akk = s[k][k];
+        if (!(akk > 0.0)) {
+            bad = k + 1;
+            break;
+        }
+        double lkk = sqrt(akk);
+        __syncthreads();
+        for (int i = k + tid; i < n; i += 256) s[i][k] = (i == k) ? lkk : s[i][k] / lkk;
+        __syncthreads();
+        int m = n - k - 1;
+        for (int idx = tid; idx < m * m; idx += 256) {
+            int ii = k + 1 + idx % m, jj = k + 1 + idx / m;
+            if (ii >= jj) s[ii][jj] -= s[ii][k] * s[jj][k];
+        }
+        __syncthreads();
+    }
+    if (bad) {
+        if (tid == 0 && flags)
+            atomicCAS(&flags[FLAG_INFO], 0ull, (unsigned long long)(col0 + bad));
+        return;
+    }
+    // inverse of the lower-triangular factor, column by column
+    if (tid < n) {
+        int j = tid;
+        for (int i = 0; i < j; ++i) x[i][j] = 0.0;
+        x[j][j] = 1.0 / s[j][j];
+        for (int i = j + 1; i < n; ++i) {
+            double acc = 0.0;
+            for (int p = j; p < i; ++p) acc += s[i][p] * x[p][j];
+            x[i][j] = -acc / s[i][i];
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < n * n; idx += 256) {
+        int i = idx % n, j = idx / n;
+        A[i + (int64_t)j * lda] = (i >= j) ? s[i][j] : 0.0;
+        T[i + (int64_t)j * ldt] = x[i][j];
+    }
+}
+
+int potrf_inv(gpex_ctx_t ctx, hipStream_t s, double* A, int64_t lda, double* T, int64_t ldt, int n,
+              double* ws, int64_t col0) {
+    auto* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
+    if (n <= LEAF) {
+        hipLaunchKernelGGL(k_potrf_leaf, dim3(1), dim3(256), 0, s, A, lda, T, ldt, n, col0, fl);
+        GPEX_HIP(ctx, hipGetLastError());
+        return GPEX_OK;
+    }
+    const int n1 = ((n / 2 + 15) / 16) * 16, n2 = n - n1;
+    double* A21 = A + n1;
+    double* A22 = A + n1 + (int64_t)n1 * lda;
+    double* T21 = T + n1;
+    double* T22 = T + n1 + (int64_t)n1 * ldt;
+    auto g = [&](const void* a, int tA, int64_t la, const void* b, int tB, int64_t lb, void* c,
+                 int64_t lc, int M, int N, int K, double al, double be) {
+        GemmTask t{};
+        t.A = a; t.B = b; t.C = c; t.lda = la; t.ldb = lb; t.ldc = lc;
+        t.M = M; t.N = N; t.K = K; t.ta = DT_F64; t.tb = DT_F64; t.tc = DT_F64;
+        t.transA = (int8_t)tA; t.transB = (int8_t)tB; t.alpha = al; t.beta = be;
+        return gemm_launch(ctx, s, DT_F64, nullptr, 1, t);
+    };
+    GPEX_TRY(potrf_inv(ctx, s, A, lda, T, ldt, n1, ws, col0));
+    // L21 = A21 T11^T (through ws: the product must not overwrite its own input)
+    GPEX_TRY(g(A21, 0, lda, T, 1, ldt, ws, n2, n2, n1, n1, 1.0, 0.0));
+    GPEX_TRY(copy2d(ctx, s, ws, DT_F64, n2, A21, DT_F64, lda, n2, n1, 1.0));
+    // A22 -= L21 L21^T
+    GPEX_TRY(g(A21, 0, lda, A21, 1, lda, A22, lda, n2, n2, n1, -1.0, 1.0));
+    GPEX_TRY(potrf_inv(ctx, s, A22, lda, T22, ldt, n2, ws, col0 + n1));
+    // T21 = -T22 (L21 T11)
+    GPEX_TRY(g(A21, 0, lda, T, 0, ldt, ws, n2, n2, n1, n1, 1.0, 0.0));
+    GPEX_TRY(g(T22, 0, ldt, ws, 0, n2, T21, ldt, n2, n1, n2, -1.0, 0.0));
+    // upper-right blocks of the factor and of its inverse are zero
+    GPEX_TRY(zero2d(ctx, s, A + (int64_t)n1 * lda, lda, n1, n2));
+    GPEX_TRY(zero2d(ctx, s, T + (int64_t)n1 * ldt, ldt, n1, n2));
+    return GPEX_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+namespace {
+struct Timer {
+    gpex_ctx_t ctx;
+    std::vector<hipEvent_t> ev;
+    size_t used = 0;
+    hipEvent_t next() {
+        if (used == ev.size()) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return nullptr;
+            ev.push_back(e);
+        }
+        return ev[used++];
+    }
+    ~Timer() {
+        for (auto e : ev) (void)hipEventDestroy(e);
+    }
+};
+}  // namespace
+
+}  // namespace gpex
+
+using namespace gpex;
+
+extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
+    if (!ctx) return GPEX_ERR_ARG;
+    if (!a || !info) return set_err(ctx, GPEX_ERR_ARG, "gpex_potrf_mp: null handle or info");
+    if (a->factored) return set_err(ctx, GPEX_ERR_STATE, "gpex_potrf_mp: matrix already factored");
+    GPEX_HIP(ctx, hipSetDevice(ctx->device));
+    const int64_t nt = a->nt;
+    const int nb = a->nb;
+    const size_t tile_el = (size_t)nb * nb;
+    hipStream_t s = ctx->stream;
+    if (!a->tinv) GPEX_TRY(dev_alloc(ctx, (void**)&a->tinv, sizeof(double) * tile_el * nt, "inverse diagonal tiles"));
+    void* pws = nullptr;
+    double* ws = nullptr;
+    if (nt > 1) GPEX_TRY(dev_alloc(ctx, &pws, 8 * tile_el * (nt - 1), "panel workspace"));
+    GPEX_TRY(dev_alloc(ctx, (void**)&ws, sizeof(double) * tile_el, "diagonal workspace"));
+    auto cleanup = [&]() {
+        dev_free(pws);
+        dev_free(ws);
+    };
+
+    // Per-step task lists, built once on the host and uploaded in one copy.
+    // Lists per step: 0 panel FP64, 1 panel FP32, 2 update FP64, 3 update FP32, 4 update FP16.
+    std::vector<GemmTask> tasks;
+    std::vector<CopyTask> copies;
+    std::vector<int64_t> list_beg((size_t)nt * 5 + 1, 0);
+    std::vector<int64_t> copy_beg((size_t)nt + 1, 0);
+    std::vector<double> upd_flops(3, 0.0);
+    for (int64_t k = 0; k < nt; ++k) {
+        for (int64_t i = k + 1; i < nt; ++i) {
+            CopyTask c{a->tile(i, k), static_cast<uint8_t*>(pws) + 8 * tile_el * (i - k - 1),
+                       (int64_t)(dt_size(a->prec(i, k)) * tile_el)};
+            copies.push_back(c);
+        }
+        copy_beg[(size_t)k + 1] = (int64_t)copies.size();
+        for (int li = 0; li < 5; ++li) {
+            list_beg[(size_t)k * 5 + li] = (int64_t)tasks.size();
+            if (li < 2) {
+                for (int64_t i = k + 1; i < nt; ++i) {
+                    int p = a->prec(i, k);
+                    if ((li == 0) != (p == DT_F64)) continue;
+                    GemmTask g{};
+                    g.A = static_cast<uint8_t*>(pws) + 8 * tile_el * (i - k - 1);
+                    g.B = a->tinv_tile(k);
+                    g.C = a->tile(i, k);
+                    g.lda = g.ldb = g.ldc = nb;
+                    g.M = g.N = g.K = nb;
+                    g.ta = (int8_t)p; g.tb = DT_F64; g.tc = (int8_t)p;
+                    g.transA = 0; g.transB = 1;
+                    g.alpha = 1.0; g.beta = 0.0;
+                    tasks.push_back(g);
+                }
+            } else {
+                int want = li - 2;
+                for (int64_t j = k + 1; j < nt; ++j)
+                    for (int64_t i = j; i < nt; ++i) {
+                        int p = (i == j) ? DT_F64 : a->prec(i, j);
+                        if (p != want) continue;
+                        GemmTask g{};
+                        g.A = a->tile(i, k);
+                        g.B = a->tile(j, k);
+                        g.C = a->tile(i, j);
+                        g.lda = g.ldb = g.ldc = nb;
+                        g.M = g.N = g.K = nb;
+                        g.ta = (int8_t)a->prec(i, k); g.tb = (int8_t)a->prec(j, k); g.tc = (int8_t)p;
+                        g.transA = 0; g.transB = 1;
+                        g.alpha = -1.0; g.beta = 1.0;
+                        tasks.push_back(g);
+                        upd_flops[want] += (i == j ? 1.0 : 2.0) * nb * (double)nb * nb;
+                    }
+            }
+        }
+    }
+    list_beg[(size_t)nt * 5] = (int64_t)tasks.size();
+    GemmTask* d_tasks = nullptr;
+    CopyTask* d_copies = nullptr;
+    if (!tasks.empty()) {
+        int r = dev_alloc(ctx, (void**)&d_tasks, sizeof(GemmTask) * tasks.size(), "task lists");
+        if (r < 0) { cleanup(); return r; }
+        (void)hipMemcpy(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice);
+    }
+    if (!copies.empty()) {
+        int r = dev_alloc(ctx, (void**)&d_copies, sizeof(CopyTask) * copies.size(), "copy lists");
+        if (r < 0) { cleanup(); dev_free(d_tasks); return r; }
+        (void)hipMemcpy(d_copies, copies.data(), sizeof(CopyTask) * copies.size(), hipMemcpyHostToDevice);
+    }
+    auto cleanup_all = [&]() {
+        cleanup();
+        dev_free(d_tasks);
+        dev_free(d_copies);
+    };
+#define POTRF_TRY(expr)                      \
+    do {                                     \
+        int r_ = (expr);                     \
+        if (r_ < 0) { cleanup_all(); return r_; } \
+    } while (0)
+
+    POTRF_TRY(hipMemsetAsync(ctx->d_flags + FLAG_INFO, 0, sizeof(long long), s) == hipSuccess
+                  ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "memset info"));
+    Timer tm{ctx};
+    struct Rec { hipEvent_t b, e; int prec; };
+    std::vector<Rec> recs;
+    hipEvent_t e_all0 = nullptr, e_all1 = nullptr;
+    if (ctx->timing) {
+        e_all0 = tm.next();
+        (void)hipEventRecord(e_all0, s);
+    }
+    for (int64_t k = 0; k < nt; ++k) {
+        POTRF_TRY(potrf_inv(ctx, s, static_cast<double*>(a->tile(k, k)), nb, a->tinv_tile(k), nb, nb, ws, k * nb));
+        if (k == nt - 1) break;
+        int64_t nc = copy_beg[(size_t)k + 1] - copy_beg[(size_t)k];
+        if (nc > 0) {
+            const int64_t chunk = 1 << 16;
+            int64_t mx = (int64_t)(8 * tile_el);
+            dim3 grid((unsigned)((mx + chunk - 1) / chunk), (unsigned)nc);
+            hipLaunchKernelGGL(k_copy_tasks, grid, dim3(256), 0, s, d_copies + copy_beg[(size_t)k], chunk);
+            POTRF_TRY(hipGetLastError() == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "panel copy launch"));
+        }
+        for (int li = 0; li < 5; ++li) {
+            int64_t b0 = list_beg[(size_t)k * 5 + li], b1 = list_beg[(size_t)k * 5 + li + 1];
+            if (b1 <= b0) continue;
+            int compute = li == 0 ? DT_F64 : li == 1 ? DT_F32 : li - 2;
+            Rec rc{nullptr, nullptr, li - 2};
+            if (ctx->timing && li >= 2) {
+                rc.b = tm.next();
+                (void)hipEventRecord(rc.b, s);
+            }
+            POTRF_TRY(gemm_launch(ctx, s, compute, d_tasks + b0, (int)(b1 - b0), tasks[(size_t)b0]));
+            if (ctx->timing && li >= 2) {
+                rc.e = tm.next();
+                (void)hipEventRecord(rc.e, s);
+                recs.push_back(rc);
+            }
+        }
+    }
+    if (ctx->timing) {
+        e_all1 = tm.next();
+        (void)hipEventRecord(e_all1, s);
+    }
+    hipError_t se = hipStreamSynchronize(s);
+    if (se != hipSuccess) {
+        cleanup_all();
+        return set_err(ctx, GPEX_ERR_HIP, std::string("potrf sync: ") + hipGetErrorString(se));
+    }
+    if (ctx->timing) {
+        float ms = 0;
+        (void)hipEventElapsedTime(&ms, e_all0, e_all1);
+        ctx->timings[0] = ms;
+        for (int p = 0; p < 3; ++p) {
+            ctx->timings[1 + 3 * p] = 0;
+            ctx->timings[2 + 3 * p] = 0;
+            ctx->timings[3 + 3 * p] = upd_flops[(size_t)p];
+        }
+        for (auto& rc : recs) {
+            float m = 0;
+            (void)hipEventElapsedTime(&m, rc.b, rc.e);
+            ctx->timings[1 + 3 * rc.prec] += m;
+            ctx->timings[2 + 3 * rc.prec] += 1;
+        }
+    }
+    long long fl = 0;
+    (void)hipMemcpy(&fl, ctx->d_flags + FLAG_INFO, sizeof(long long), hipMemcpyDeviceToHost);
+    cleanup_all();
+    *info = fl;
+    a->factored = true;
+    if (fl != 0) {
+        a->factored = false;
+        return set_err(ctx, GPEX_ERR_NOT_SPD, "gpex_potrf_mp: non-positive pivot at column " + std::to_string(fl));
+    }
+    return GPEX_OK;
+}

@@ -1,0 +1,118 @@
+// Internal declarations shared by the gfx950 HIP sources of libgpex.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "gpex.h"
+
+namespace gpex {
+
+// Storage / compute precision codes (same numbering as the public precision map).
+enum : int { DT_F64 = 0, DT_F32 = 1, DT_F16 = 2 };
+inline size_t dt_size(int dt) { return dt == DT_F64 ? 8 : (dt == DT_F32 ? 4 : 2); }
+
+// Device-side flag words kept per context (zeroed by the entry points that use them).
+enum : int { FLAG_INFO = 0, FLAG_FP16_OVF = 1, FLAG_MSPE = 2, FLAG_COUNT = 4 };
+
+}  // namespace gpex
+
+struct gpex_ctx_s {
+    int device = 0;
+    hipStream_t stream = nullptr;
+    std::string err;
+    long long* d_flags = nullptr;     // FLAG_COUNT device words
+    bool timing = false;
+    hipEvent_t ev[8] = {};
+    double timings[6] = {0, 0, 0, 0, 0, 0};
+};
+
+struct gpex_tiled_s {
+    int device = 0;
+    int64_t n = 0, nt = 0;
+    int nb = 0;
+    std::vector<uint8_t> map;        // nt*nt, row-major, 255 above the diagonal
+    std::vector<int64_t> off;        // byte offset of lower tile t = i(i+1)/2 + j in `base`
+    uint8_t* base = nullptr;         // tile storage, each tile nb x nb column-major
+    size_t bytes = 0;
+    double s = 1.0;
+    std::vector<double> stats;       // 3 per lower tile: sum of squares, min, max (unscaled)
+    double* tinv = nullptr;          // nt tiles nb x nb FP64: inverse of each diagonal factor tile
+    bool factored = false;
+    gpex_prec_opts opts{};
+    gpex_diag diag{};
+
+    int64_t tidx(int64_t i, int64_t j) const { return i * (i + 1) / 2 + j; }
+    int prec(int64_t i, int64_t j) const { return map[(size_t)(i * nt + j)]; }
+    void* tile(int64_t i, int64_t j) const { return base + off[(size_t)tidx(i, j)]; }
+    double* tinv_tile(int64_t k) const { return tinv + (size_t)k * nb * nb; }
+};
+
+namespace gpex {
+
+int set_err(gpex_ctx_t ctx, int code, const std::string& msg);
+
+#define GPEX_HIP(ctx, call)                                                                 \
+    do {                                                                                    \
+        hipError_t e_ = (call);                                                             \
+        if (e_ != hipSuccess)                                                               \
+            return ::gpex::set_err((ctx), GPEX_ERR_HIP,                                     \
+                                   std::string(#call) + ": " + hipGetErrorString(e_));      \
+    } while (0)
+
+#define GPEX_TRY(expr)               \
+    do {                             \
+        int r_ = (expr);             \
+        if (r_ < 0) return r_;       \
+    } while (0)
+
+int dev_alloc(gpex_ctx_t ctx, void** p, size_t bytes, const char* what);
+void dev_free(void* p);
+
+// ---- batched mixed-precision GEMM engine (gemm.hip) ---------------------------------------
+// One task: C (M x N) = alpha * op(A) * op(B) + beta * C.  op(A) is M x K, op(B) is K x N.
+// Storage codes ta/tb/tc pick each operand's element type; trans flags pick the layout:
+// transA = 0: A(m, k) at A[m + k*lda]; transA = 1: A(m, k) at A[k + m*lda];
+// transB = 0: B(k, n) at B[k + n*ldb]; transB = 1: B(k, n) at B[n + k*ldb].
+// With beta == 0 the old C is not read.
+struct GemmTask {
+    const void* A;
+    const void* B;
+    void* C;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    int8_t ta, tb, tc, transA, transB, pad0, pad1, pad2;
+    double alpha, beta;
+};
+
+// compute: DT_F64 (FP64 matrix cores), DT_F32 (FP32 matrix cores) or DT_F16 (FP16 matrix cores,
+// FP32 accumulation).  Either `d_tasks` (device array of ntasks tasks with identical M, N, K) or,
+// when d_tasks is null, the single task `one` passed by value.
+int gemm_launch(gpex_ctx_t ctx, hipStream_t s, int compute, const GemmTask* d_tasks, int ntasks,
+                const GemmTask& one);
+
+// Convenience: single-task GEMM on the context stream.
+int gemm1(gpex_ctx_t ctx, int compute, const void* A, int ta, int transA, int64_t lda,
+          const void* B, int tb, int transB, int64_t ldb, void* C, int tc, int64_t ldc, int M,
+          int N, int K, double alpha, double beta);
+
+// ---- small helpers (chol.hip) ---------------------------------------------------------------
+// Dense 2-D copy with element-type conversion (RNE on narrowing; FP16 overflow sets the flag).
+int copy2d(gpex_ctx_t ctx, hipStream_t s, const void* src, int tsrc, int64_t lds, void* dst,
+           int tdst, int64_t ldd, int64_t rows, int64_t cols, double scale);
+// Set a rows x cols FP64 block to zero.
+int zero2d(gpex_ctx_t ctx, hipStream_t s, double* dst, int64_t ldd, int64_t rows, int64_t cols);
+
+// Factor the FP64 diagonal block A (n x n, leading dim lda) in place (lower, upper zeroed) and
+// write its inverse into T (n x n, leading dim ldt, upper zeroed).  ws: FP64 scratch of at least
+// n*n/4 elements + n*n (leading dim n).  col0 is the global 0-based column of A(0,0) (for info).
+int potrf_inv(gpex_ctx_t ctx, hipStream_t s, double* A, int64_t lda, double* T, int64_t ldt,
+              int n, double* ws, int64_t col0);
+
+// ---- planner (planner.cpp) -------------------------------------------------------------------
+void plan_precision(const std::vector<double>& stats, int64_t nt, const gpex_prec_opts& o,
+                    std::vector<uint8_t>& map, gpex_diag& d);
+
+}  // namespace gpex

@@ -1,0 +1,216 @@
+/*
+ * gpex.h -- C ABI of the MI355X (gfx950) excursion-set simulation library.
+ *
+ * The library computes, on one GPU, the hot path of the workflow described in
+ * "Mixed-Precision GPU Acceleration for Confidence Regions of Spatial Excursion Sets"
+ * (Zhang, Abdulah, Cao, French, Alomairy, Genton, Keyes):
+ *   covariance tile generation and per-tile statistics         (Sec. V, Eq. 4; Sec. V-D)
+ *   precision plan: tile map, Eq. 10/11 checks, scale s        (Sec. IV-B, V-D, V-E, Eq. 12)
+ *   adaptive mixed-precision tile Cholesky of s^2 V            (Sec. IV-B; Algorithm 2, step 12)
+ *   standard normals, compensation B = Z/s, TRMM M = L_s B     (Sec. IV-C, Eq. 3; Algorithm 1)
+ *   universal kriging weights, predictor and MSPE              (Sec. V-A, Eq. 5, Eq. 6)
+ *   conditioning, exceedance/extrema scan, calibration         (Sec. V-B, Eq. 7; V-C, Eq. 8, 9)
+ *
+ * Conventions (all entry points):
+ *   - Pointers named d_* are device pointers owned by the caller (for example torch tensors
+ *     on the context's device); pointers named h_* are host pointers owned by the caller.
+ *     The library never frees caller memory.
+ *   - Matrices are column-major with an explicit leading dimension; vectors are contiguous.
+ *   - All device work is enqueued on the stream given at context creation.  Entry points that
+ *     return host values (info, diagnostics, psi/phi, region statistics) synchronise that
+ *     stream before returning; gpex_cov_gen also synchronises (the precision plan needs the
+ *     tile statistics on the host).
+ *   - Return value: GPEX_OK (0); a negative code for misuse or a HIP failure (message via
+ *     gpex_last_error); a positive code for a numerical condition the method names.
+ *   - The library does not reorder locations: callers pass them in the order they want the
+ *     tiles to follow (a space-filling order keeps near-diagonal tiles strongly correlated).
+ *   - A context and the objects created through it are not thread-safe.
+ *
+ * Precision codes used in maps: 0 = FP64, 1 = FP32, 2 = FP16 (255 above the diagonal).
+ */
+#ifndef GPEX_H
+#define GPEX_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gpex_ctx_s* gpex_ctx_t;
+typedef struct gpex_tiled_s* gpex_tiled_t;
+
+typedef enum {
+    GPEX_OK = 0,
+    GPEX_ERR_ARG = -1,           /* invalid argument (message names it) */
+    GPEX_ERR_HIP = -2,           /* a HIP runtime call failed */
+    GPEX_ERR_NOMEM = -3,         /* device allocation failed */
+    GPEX_ERR_STATE = -4,         /* object in the wrong state (e.g. TRMM of an unfactored matrix) */
+    GPEX_ERR_NOT_SPD = 1,        /* Cholesky met a non-positive pivot; info holds the column */
+    GPEX_ERR_MSPE_NONPOS = 2,    /* some v_i <= 0: Sec. V-C requires positive MSPEs */
+    GPEX_ERR_EMPTY_SAMPLE = 3,   /* psi or phi sample empty: Sec. V-C needs both non-empty */
+    GPEX_WARN_CHECKS_FAILED = 4, /* Eq. 10 or Eq. 11 failed under a user tolerance (reported only) */
+    GPEX_WARN_FP16_OVERFLOW = 5  /* a value stored in FP16 rounded to +-inf */
+} gpex_status;
+
+/* Covariance model.  kind 0: Matern with nu in {0.5, 1.5, 2.5} and distance scaled by the range
+ * (r = d / range): sigma2 e^-r, sigma2 (1 + r) e^-r, sigma2 (1 + r + r^2/3) e^-r.
+ * kind 1: Gaussian sigma2 exp(-d^2 / range) ("Massively parallel approximate Gaussian process
+ * regression", isotropic Gaussian correlation).  d is the Euclidean distance in the plane.
+ * nugget is added to every diagonal entry unless a per-location diagonal is given. */
+typedef struct {
+    int kind;
+    double sigma2, range, nu, nugget;
+} gpex_cov_params;
+
+/* Precision options.  amp = 0: every tile FP64 and s = 1 (Algorithm 1, AMP = 0 branch).
+ * amp = 1: off-diagonal tile (i, j) with r = ||V_ij||_F / ||V||_F goes to FP16 when allow_fp16
+ * and r * 2^-10 <= tol, else to FP32 when r * 2^-23 <= tol, else stays FP64 (nt_rule != 0
+ * multiplies r by the tile count first).  tol is the pages' fixedacc. */
+typedef struct {
+    int amp;
+    double tol;
+    int allow_fp16;
+    int nt_rule;
+} gpex_prec_opts;
+
+/* Diagnostics of the plan (Sec. V-D, V-E) and of the simulation input (Algorithm 1). */
+typedef struct {
+    double s;             /* applied covariance scale, Eq. 12 (1 when unscaled) */
+    double frob;          /* ||V||_F of the unscaled matrix */
+    double l_bound;       /* l = max_f l_f (normal-range lower bound) */
+    double u_bound;       /* u_s = min(65504, min_f u_f) */
+    double l_bound_sub;   /* lower bound with the subnormal limits (reported when l > u_s) */
+    double r_hp;          /* Eq. 10 ratio v_max^HP / v_min^HP (NaN without FP16 tiles) */
+    double rho1, rho2;    /* Eq. 11 ratios */
+    double norm_B;        /* ||Z / s||_F of the simulation input (gpex_trmm_sim) */
+    int eq10_pass, eq11_pass, lower_exceeds_upper, fp16_overflow;
+    int64_t tiles[3];     /* lower tiles per precision: FP64, FP32, FP16 */
+} gpex_diag;
+
+typedef struct {
+    double q_in, q_out;   /* critical values q_in = Q_{1-alpha}(phi), q_out = Q_alpha(psi) */
+    int64_t n_psi, n_phi; /* sample sizes after dropping empty-set sentinels */
+} gpex_region_stats;
+
+/* ---- context ------------------------------------------------------------------------------ */
+/* Binds HIP device `device` and the stream `hip_stream` (a hipStream_t; NULL = null stream).
+ * *out receives the context.  Errors: GPEX_ERR_ARG, GPEX_ERR_HIP. */
+int gpex_ctx_create(int device, void* hip_stream, gpex_ctx_t* out);
+int gpex_ctx_destroy(gpex_ctx_t ctx);
+/* Text of the last non-OK status on this context (valid until the next call on it). */
+const char* gpex_last_error(gpex_ctx_t ctx);
+/* Library version string. */
+const char* gpex_version(void);
+
+/* ---- covariance generation + precision plan -------------------------------------------- */
+/* Generates the n x n covariance of the locations d_loc (SoA: x in d_loc[0..n), y in
+ * d_loc[n..2n)), Eq. 4 of the mixed-precision page (joint covariance, prediction rows first
+ * when the caller orders them so).  The diagonal gets d_diag_add[i] when d_diag_add is not
+ * NULL (this is how tau^2 enters only the observation rows), else params->nugget.
+ * The matrix is cut into nb x nb tiles (NT = ceil(n / nb), last tile padded with an identity
+ * diagonal and zeros).  Pass 1 computes per-tile sum of squares, minimum and maximum of the
+ * unscaled entries; the host plans the precision map and s (Sec. V-D, V-E); pass 2 writes
+ * s^2 V_ij of each lower tile in its precision (round to nearest even).
+ * *out receives a library-owned tiled matrix (release with gpex_tiled_destroy).
+ * diag may be NULL.  Synchronises.  Returns GPEX_OK, GPEX_WARN_CHECKS_FAILED (Eq. 10/11 failed:
+ * results still produced), GPEX_WARN_FP16_OVERFLOW, or an error.
+ * Constraints: n >= 1, 16 <= nb <= 2048 and nb % 16 == 0. */
+int gpex_cov_gen(gpex_ctx_t ctx, const double* d_loc, int64_t n, const double* d_diag_add,
+                 const gpex_cov_params* params, int nb, const gpex_prec_opts* opts,
+                 gpex_tiled_t* out, gpex_diag* diag);
+
+/* Host-only planning from tile statistics (no device work): h_stats holds 3*nt*(nt+1)/2 doubles
+ * (sum of squares, min, max per lower tile, row-packed), h_map receives nt*nt bytes (row-major,
+ * 255 above the diagonal), diag the Eq. 10/11 values and the Eq. 12 scale.  This is the plan
+ * gpex_cov_gen applies; it lets a caller re-plan cached statistics under another tolerance.
+ * Returns GPEX_OK or GPEX_ERR_ARG. */
+int gpex_plan(const double* h_stats, int64_t nt, const gpex_prec_opts* opts, uint8_t* h_map,
+              gpex_diag* diag);
+
+/* Sizes, map and scale of a tiled matrix.  h_map (NT*NT bytes, row-major, may be NULL). */
+int gpex_tiled_info(gpex_tiled_t t, int64_t* n, int* nb, int64_t* nt, uint8_t* h_map, double* s);
+/* Per-tile statistics of the unscaled matrix, 3 doubles per lower tile (sum of squares, min,
+ * max) in row-packed order t = i(i+1)/2 + j.  h_stats holds 3*NT*(NT+1)/2 doubles. */
+int gpex_tiled_stats(gpex_tiled_t t, double* h_stats);
+/* Copies the stored lower tiles, converted to FP64 and unscaled (divided by s^2 before the
+ * factorisation and by s after it, so a matrix reads as V and a factor as chol(V)), into the
+ * dense n x n column-major d_out (leading dimension ld >= n); entries above the diagonal tiles
+ * are set to 0.  Enqueued on ctx. */
+int gpex_tiled_to_dense(gpex_ctx_t ctx, gpex_tiled_t t, double* d_out, int64_t ld);
+int gpex_tiled_destroy(gpex_tiled_t t);
+
+/* ---- mixed-precision tile Cholesky ------------------------------------------------------- */
+/* Factors the tiled matrix in place: s^2 V = L_s L_s^T, keeping the precision map (diagonal
+ * POTRF in FP64; a panel tile is solved in its own precision, FP16 tiles computed in FP32;
+ * a trailing tile is updated in its own precision with operands converted to it; FP16 updates
+ * use FP16 matrix cores with FP32 accumulation).  *info = 0, or the 1-based column of the first
+ * non-positive pivot (then GPEX_ERR_NOT_SPD).  Synchronises. */
+int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info);
+
+/* ---- simulation --------------------------------------------------------------------------- */
+/* Standard normals of the seeded counter-based generator into d_Z (n x nsim, leading dim ld):
+ * element (i, j) has linear index l = j n + i, pair p = l / 2, Philox4x32-10 counter
+ * (p mod 2^32, p / 2^32, stream, 0) and key (seed mod 2^32, seed / 2^32); u1 from output words
+ * 0-1, u2 from words 2-3 as ((w >> 11) + 1/2) 2^-53; Z_2p = sqrt(-2 ln u1) cos(2 pi u2),
+ * Z_2p+1 = sqrt(-2 ln u1) sin(2 pi u2).  Enqueued on ctx. */
+int gpex_normals(gpex_ctx_t ctx, uint64_t seed, uint32_t stream, int64_t n, int64_t nsim,
+                 double* d_Z, int64_t ld);
+
+/* M = L_s B with B = Z / s (Algorithm 1 and Eq. 3 of the mixed-precision page).  Z is either
+ * the explicit d_Z (n x nsim, leading dimension n) or, when d_Z is NULL, the seeded normals of
+ * gpex_normals(seed, stream 0).  With amp = 1, B is rounded to FP16, each off-diagonal L tile
+ * is converted to FP16 and multiplied on FP16 matrix cores, the diagonal tile is applied in
+ * FP32, all with FP32 accumulation, and M is written in FP64; with amp = 0 everything is FP64.
+ * d_M: n x nsim, leading dimension ldm >= n.  diag (may be NULL) receives norm_B.
+ * Requires a factored matrix (GPEX_ERR_STATE otherwise).  Synchronises when diag != NULL. */
+int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t l, int64_t nsim, uint64_t seed, const double* d_Z,
+                  double* d_M, int64_t ldm, gpex_diag* diag);
+
+/* ---- universal kriging -------------------------------------------------------------------- */
+/* Universal kriging (Sec. V-A, Eq. 5, Eq. 6) with trend design rows (1, x, y) when k_trend = 3
+ * (k_trend = 0: no trend).  Sigma_y = V_o + tau2 I is factored in FP64 tiles of size nb;
+ * W = Sigma_y^-1 [V_op - X_o H] via the retained factor, zhat = W^T y_o and
+ * v_i = sigma2 + w_i^T Sigma_y w_i - 2 w_i^T c_i, evaluated with Sigma_y W = V_op - X_o H.
+ * d_loc_o (2*n_o, SoA), d_loc_p (2*n_p, SoA), d_y_o (n_o).  Outputs: d_W (n_o x n_p,
+ * leading dimension n_o), d_zhat (n_p), d_v (n_p).  params->nugget is ignored (tau2 is the
+ * observation-block diagonal).  *info as in gpex_potrf_mp (-1: trend system not SPD).
+ * Synchronises. */
+int gpex_krige(gpex_ctx_t ctx, const double* d_loc_o, int64_t n_o, const double* d_loc_p,
+               int64_t n_p, const double* d_y_o, int k_trend, const gpex_cov_params* params,
+               double tau2, int nb, double* d_W, double* d_zhat, double* d_v, int64_t* info);
+
+/* ---- conditioning, exceedances and confidence regions ----------------------------------- */
+/* S = M_p + W^T (y_o 1^T - M_o) (Eq. 7; with n_o = 0, S = M), then the fused scan of Eq. 8:
+ *   d_counts[i] = #{j : S_ij >= u} (int64, n_p), d_sizes[j] = #{i : S_ij >= u} (int32, nsim).
+ * When d_zhat and d_v are given: t = (zhat - u) / sqrt(v) (Eq. 1), psi_j = min of t over
+ * {S_ij >= u} (+inf if empty), phi_j = max of t over {S_ij <= u} (-inf if empty) into h_psi,
+ * h_phi (host, nsim); samples without sentinels, q_out = Q_{1-c}(psi), q_in = Q_c(phi) with
+ * Eq. 9 (p read as a six-place decimal, exact integer ceiling); d_cout[i] = t_i >= q_out,
+ * d_cin[i] = t_i > q_in (uint8, n_p); st receives q_in, q_out, n_psi, n_phi.
+ * d_M: (n_p + n_o) x nsim, leading dimension ldm, prediction rows first.  d_W (n_o x n_p, ld
+ * n_o) and d_y_o are needed when n_o > 0.  d_S (may be NULL) receives S (n_p x nsim, ld n_p).
+ * Returns GPEX_ERR_MSPE_NONPOS when some v_i <= 0 and GPEX_ERR_EMPTY_SAMPLE when a sample is
+ * empty (counts and psi/phi are still written).  Synchronises when d_zhat is given. */
+int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p,
+                           int64_t n_o, int64_t nsim, const double* d_W, const double* d_y_o,
+                           const double* d_zhat, const double* d_v, double u, double level_c,
+                           int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
+                           uint8_t* d_cin, uint8_t* d_cout, double* d_S, gpex_region_stats* st);
+
+/* ---- timing support ------------------------------------------------------------------------ */
+/* Per-phase device time of the last gpex_potrf_mp / gpex_trmm_sim on ctx, measured with HIP
+ * events recorded on the context stream around the launches (enable with
+ * gpex_ctx_set_timing(ctx, 1); it adds event records and no synchronisation).  out[16]:
+ *   [0] potrf total ms;
+ *   [1..3] trailing-update launches computing in FP64: summed ms, launch count, algorithmic flops
+ *          (2 nb^3 per off-diagonal tile, nb^3 per diagonal tile);
+ *   [4..6] the same for FP32 launches, [7..9] for FP16 launches;
+ *   [10] trmm total ms, [11] trmm matrix-core launches ms; [12..15] reserved (0). */
+int gpex_ctx_set_timing(gpex_ctx_t ctx, int on);
+int gpex_ctx_timings(gpex_ctx_t ctx, double* out16);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPEX_H */

@@ -1,0 +1,299 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances: all-FP64 path relative Frobenius 1e-10 and bit-exact integer exceedance counts;
+mixed-precision path 5e-3 for the factor and 1e-2 for simulated fields (relative Frobenius).
+Sizes span several tiles with a ragged last tile.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import gpex_synth as syn
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU but skipped there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import gp_conditional_simulation_amd as g  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def ctx():
+    c = g.Context(0)
+    yield c
+    c.close()
+
+
+def rel(a, b):
+    return float(np.linalg.norm(np.asarray(a) - np.asarray(b)) / np.linalg.norm(np.asarray(b)))
+
+
+def dev(a):
+    return torch.tensor(np.ascontiguousarray(a), dtype=torch.float64, device="cuda:0")
+
+
+def dev_cm(a):
+    """Column-major device copy of a 2-D numpy array (view n x m)."""
+    return torch.tensor(np.ascontiguousarray(np.asarray(a).T), dtype=torch.float64, device="cuda:0").T
+
+
+def setup_case(n, nb, nu, beta, seed, nugget=1e-4, grid=0):
+    if grid:
+        x, y = syn.grid_centres(grid)
+    else:
+        x, y = syn.uniform_locations(n, seed)
+    x, y, _ = syn.ordered_locations(x, y)
+    params = {"kind": 0, "sigma2": 1.0, "range": beta, "nu": nu, "nugget": nugget}
+    return x, y, params
+
+
+CASES_FP64 = [
+    # (n, nb, nu, beta, seed, grid): several tiles, ragged last tile, the 40 x 40 grid workload
+    (1600, 160, 0.5, 0.1, 0, 40),
+    (1000, 160, 1.5, 0.1, 3, 0),
+    (777, 128, 2.5, 0.05, 4, 0),
+    (2500, 256, 1.5, 0.3, 5, 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES_FP64, ids=lambda c: f"n{c[0]}_nb{c[1]}_nu{c[2]}")
+def test_cov_gen_stats_and_values(ctx, case):
+    n, nb, nu, beta, seed, grid = case
+    x, y, params = setup_case(n, nb, nu, beta, seed, grid=grid)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=0)
+    V = oracle.cov_matrix(x, y, 0, 1.0, beta, nu, nugget=1e-4)
+    Vg = A.to_dense().cpu().numpy()
+    np.testing.assert_allclose(np.tril(Vg), np.tril(V), rtol=1e-13, atol=1e-300)
+    st_g = A.stats()
+    st_o = oracle.tile_stats(V, nb)
+    np.testing.assert_allclose(st_g[:, 0], st_o[:, 0], rtol=1e-12)
+    np.testing.assert_allclose(st_g[:, 1:], st_o[:, 1:], rtol=1e-13)
+    A.close()
+
+
+@pytest.mark.parametrize("tol", [1e-9, 1e-6, 1e-3])
+def test_plan_from_device_stats_matches_oracle_plan(ctx, tol):
+    n, nb = 3000, 160
+    x, y, params = setup_case(n, nb, 1.5, 0.03, 12)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=tol)
+    info = A.info()
+    r = oracle.plan(A.stats(), info["nt"], tol)
+    low = np.tril_indices(info["nt"])
+    assert np.array_equal(info["map"][low], r.pmap[low])
+    assert info["s"] == r.s and A.diag["s"] == r.s
+    assert list(A.diag["tiles"]) == list(r.tiles)
+    # stored values: each tile within its precision's rounding of s^2 V (then unscaled)
+    V = oracle.cov_matrix(x, y, 0, 1.0, 0.03, 1.5, nugget=1e-4)
+    Vg = A.to_dense().cpu().numpy()
+    nt = info["nt"]
+    for i in range(nt):
+        for j in range(i + 1):
+            a = Vg[i * nb:(i + 1) * nb, j * nb:(j + 1) * nb]
+            b = V[i * nb:(i + 1) * nb, j * nb:(j + 1) * nb]
+            p = info["map"][i, j]
+            eps = {0: 3e-14, 1: 2.0 ** -24 + 3e-14, 2: 2.0 ** -11 + 3e-14}[p]  # exp(-d/beta) amplifies a 1-ulp distance change by d/beta (<= 47 here)
+            floor = {0: 0.0, 1: 0.0, 2: 2.0 ** -24 / r.s ** 2}[p]
+            assert np.all(np.abs(a - b) <= eps * np.abs(b) * 1.0001 + floor * 0.5001 + 1e-300), (i, j, p)
+    A.close()
+
+
+@pytest.mark.parametrize("case", CASES_FP64, ids=lambda c: f"n{c[0]}_nb{c[1]}_nu{c[2]}")
+def test_potrf_fp64(ctx, case):
+    n, nb, nu, beta, seed, grid = case
+    x, y, params = setup_case(n, nb, nu, beta, seed, grid=grid)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=0)
+    assert g.potrf_mp(ctx, A) == 0
+    L = A.to_dense().cpu().numpy()
+    V = oracle.cov_matrix(x, y, 0, 1.0, beta, nu, nugget=1e-4)
+    Lo, info = oracle.potrf(V)
+    assert info == 0
+    assert np.all(np.triu(L, 1) == 0)
+    assert rel(L, Lo) <= 1e-10, rel(L, Lo)
+    assert rel(L @ L.T, V) <= 1e-12
+    A.close()
+
+
+def test_potrf_reports_non_spd(ctx):
+    # a negative diagonal entry at location 150 makes the pivot of column 151 negative
+    n, nb = 300, 64
+    x, y = syn.uniform_locations(n, 1)
+    da = np.full(n, 1e-4)
+    da[150] = -1.5
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, {"kind": 0, "sigma2": 1.0, "range": 0.1, "nu": 0.5, "nugget": 0.0},
+                  nb, amp=0, diag_add=dev(da))
+    info = g.potrf_mp(ctx, A)
+    V = oracle.cov_matrix(x, y, 0, 1.0, 0.1, 0.5, diag_add=da)
+    _, info_o = oracle.potrf(V)
+    assert info == info_o == 151
+    A.close()
+
+
+MP_CASES = [
+    # (n, nb, nu, beta, seed, tol)
+    (3200, 320, 1.5, 0.03, 1002, 1e-9),
+    (3200, 320, 1.5, 0.1, 1002, 1e-9),
+    (3200, 320, 1.5, 0.3, 1002, 1e-9),
+    (4000, 512, 2.5, 0.1, 1003, 1e-6),
+    (4000, 512, 2.5, 0.1, 1003, 1e-8),
+]
+
+
+@pytest.mark.parametrize("case", MP_CASES, ids=lambda c: f"n{c[0]}_b{c[3]}_tol{c[5]:g}")
+def test_potrf_and_trmm_mixed_precision(ctx, case):
+    n, nb, nu, beta, seed, tol = case
+    x, y, params = setup_case(n, nb, nu, beta, seed)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=tol)
+    assert g.potrf_mp(ctx, A) == 0
+    L = A.to_dense().cpu().numpy()
+    V = oracle.cov_matrix(x, y, 0, 1.0, beta, nu, nugget=1e-4)
+    Lo, _ = oracle.potrf(V)
+    ef = rel(L, Lo)
+    nsim = 200
+    Z = syn.explicit_normals(n, nsim, seed + 1)
+    M, d = g.trmm_sim(ctx, A, nsim, Z=dev_cm(Z))
+    Mo = oracle.trmm(Lo, Z)
+    em = rel(M.cpu().numpy(), Mo)
+    print(f"map {A.diag['tiles']} s {A.diag['s']} factor {ef:.3e} M {em:.3e} normB {d['norm_B']:.4e}")
+    assert ef <= 5e-3
+    assert em <= 1e-2
+    assert d["norm_B"] == pytest.approx(np.linalg.norm(Z) / A.diag["s"], rel=1e-12)
+    A.close()
+
+
+def test_loose_tolerance_reports_failed_checks(ctx):
+    # tol 1e-4 sends even the tiles beside the diagonal to FP16: Eq. 11 fails and, with a user
+    # tolerance, the failure is reported (Sec. V-D) while the factorisation still runs
+    n, nb = 2000, 160
+    x, y, params = setup_case(n, nb, 1.5, 0.03, 9)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=1e-4)
+    assert A.status == g.WARN_CHECKS_FAILED
+    assert not A.diag["eq11_pass"]
+    r = oracle.plan(A.stats(), A.info()["nt"], 1e-4)
+    assert not r.eq11_pass and A.diag["tiles"] == list(r.tiles)
+    assert g.potrf_mp(ctx, A) >= 0
+    A.close()
+
+
+@pytest.mark.parametrize("case", CASES_FP64, ids=lambda c: f"n{c[0]}_nb{c[1]}_nu{c[2]}")
+def test_trmm_fp64_counts_bit_exact(ctx, case):
+    n, nb, nu, beta, seed, grid = case
+    x, y, params = setup_case(n, nb, nu, beta, seed, grid=grid)
+    nsim, u = 100, 0.5
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=0)
+    assert g.potrf_mp(ctx, A) == 0
+    Z = syn.explicit_normals(n, nsim, 2001)
+    M, _ = g.trmm_sim(ctx, A, nsim, Z=dev_cm(Z))
+    V = oracle.cov_matrix(x, y, 0, 1.0, beta, nu, nugget=1e-4)
+    Lo, _ = oracle.potrf(V)
+    Mo = oracle.trmm(Lo, Z)
+    Mg = M.cpu().numpy()
+    assert rel(Mg, Mo) <= 1e-10
+    out = g.excursion_regions(ctx, M, n, 0, nsim, u)
+    so = oracle.scan(Mo, u)
+    near = np.sum(np.abs(Mo - u) < 1e-9)
+    assert near == 0, f"{near} near-ties |S-u| < 1e-9 (diagnostic)"
+    assert np.array_equal(out["counts"].cpu().numpy(), so["counts"])
+    assert np.array_equal(out["sizes"].cpu().numpy(), so["sizes"])
+    A.close()
+
+
+def test_seeded_normals_match_oracle_generator(ctx):
+    n, nsim = 1001, 37
+    Zg = g.normals(ctx, 2001, 0, n, nsim).cpu().numpy()
+    Zo = oracle.normals(2001, 0, n, nsim)
+    np.testing.assert_allclose(Zg, Zo, rtol=4e-15, atol=4e-15)
+    Zg1 = g.normals(ctx, 77, 3, n, nsim).cpu().numpy()
+    np.testing.assert_allclose(Zg1, oracle.normals(77, 3, n, nsim), rtol=4e-15, atol=4e-15)
+
+
+def test_seeded_trmm_uses_the_seeded_stream(ctx):
+    n, nb, nsim = 640, 160, 50
+    x, y, params = setup_case(n, nb, 0.5, 0.1, 0)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=0)
+    assert g.potrf_mp(ctx, A) == 0
+    M, _ = g.trmm_sim(ctx, A, nsim, seed=2001)
+    Lo, _ = oracle.potrf(oracle.cov_matrix(x, y, 0, 1.0, 0.1, 0.5, nugget=1e-4))
+    Mo = oracle.trmm(Lo, oracle.normals(2001, 0, n, nsim))
+    assert rel(M.cpu().numpy(), Mo) <= 1e-10
+    A.close()
+
+
+def _krige_case(n_o, n_p, seed, tau2=0.01, beta=0.1, nu=1.5):
+    xo, yo = syn.uniform_locations(n_o, seed)
+    xp, yp = syn.uniform_locations(n_p, seed + 100)
+    xo, yo, _ = syn.ordered_locations(xo, yo)
+    xp, yp, _ = syn.ordered_locations(xp, yp)
+    rng = np.random.default_rng(seed)
+    y_obs = syn.trend_mean(xo, yo, (0.5, 1.0, -1.0)) + rng.standard_normal(n_o)
+    return xo, yo, xp, yp, y_obs
+
+
+@pytest.mark.parametrize("k_trend", [3, 0])
+@pytest.mark.parametrize("n_o,n_p,nb", [(1500, 700, 256), (1000, 1000, 160)])
+def test_krige_fp64(ctx, k_trend, n_o, n_p, nb):
+    xo, yo, xp, yp, y_obs = _krige_case(n_o, n_p, 4)
+    params = {"kind": 0, "sigma2": 1.0, "range": 0.1, "nu": 1.5}
+    W, zhat, v, info = g.krige(ctx, dev(np.r_[xo, yo]), n_o, dev(np.r_[xp, yp]), n_p, dev(y_obs), k_trend, params,
+                               0.01, nb)
+    assert info == 0
+    r = oracle.krige(xo, yo, xp, yp, y_obs, k_trend, 0, 1.0, 0.1, 1.5, 0.01)
+    Wg = W.cpu().numpy()
+    assert rel(Wg, r["W"]) <= 1e-10
+    assert rel(zhat.cpu().numpy(), r["zhat"]) <= 1e-10
+    assert rel(v.cpu().numpy(), r["v"]) <= 1e-10
+    if k_trend:
+        Xo, Xp = syn.design_matrix(xo, yo), syn.design_matrix(xp, yp)
+        np.testing.assert_allclose(Xo.T @ Wg, Xp.T, atol=1e-9)
+
+
+def test_conditioning_scan_and_regions(ctx):
+    n_o, n_p, nb, nsim, u, c = 1200, 800, 256, 300, 1.0, 0.9
+    xo, yo, xp, yp, y_obs = _krige_case(n_o, n_p, 21)
+    params = {"kind": 0, "sigma2": 1.0, "range": 0.1, "nu": 1.5}
+    W, zhat, v, info = g.krige(ctx, dev(np.r_[xo, yo]), n_o, dev(np.r_[xp, yp]), n_p, dev(y_obs), 3, params, 0.01, nb)
+    assert info == 0
+    x = np.r_[xp, xo]; y = np.r_[yp, yo]
+    diag_add = np.r_[np.zeros(n_p), np.full(n_o, 0.01)]
+    n = n_p + n_o
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, dict(params, nugget=0.0), nb, amp=0, diag_add=dev(diag_add))
+    assert g.potrf_mp(ctx, A) == 0
+    Z = syn.explicit_normals(n, nsim, 2004)
+    M, _ = g.trmm_sim(ctx, A, nsim, Z=dev_cm(Z))
+    out = g.excursion_regions(ctx, M, n_p, n_o, nsim, u, c, W=W, y_o=dev(y_obs), zhat=zhat, v=v, want_S=True)
+    assert out["status"] == 0
+    # oracle chain
+    r = oracle.krige(xo, yo, xp, yp, y_obs, 3, 0, 1.0, 0.1, 1.5, 0.01)
+    V = oracle.cov_matrix(x, y, 0, 1.0, 0.1, 1.5, diag_add=diag_add)
+    Lo, _ = oracle.potrf(V)
+    So = oracle.condition(oracle.trmm(Lo, Z), n_p, r["W"], y_obs)
+    assert rel(out["S"].cpu().numpy(), So) <= 1e-10
+    t = (r["zhat"] - u) / np.sqrt(r["v"])
+    sc = oracle.scan(So, u, t)
+    assert np.sum(np.abs(So - u) < 1e-9) == 0
+    assert np.array_equal(out["counts"].cpu().numpy(), sc["counts"])
+    assert np.array_equal(out["sizes"].cpu().numpy(), sc["sizes"])
+    np.testing.assert_allclose(out["psi"], sc["psi"], rtol=1e-9)
+    np.testing.assert_allclose(out["phi"], sc["phi"], rtol=1e-9)
+    cal = oracle.calibrate(sc["psi"], sc["phi"], t, c)
+    assert out["n_psi"] == cal["n_psi"] and out["n_phi"] == cal["n_phi"]
+    assert out["q_out"] == pytest.approx(cal["q_out"], rel=1e-9)
+    assert out["q_in"] == pytest.approx(cal["q_in"], rel=1e-9)
+    assert np.array_equal(out["cout"].cpu().numpy(), cal["cout"])
+    assert np.array_equal(out["cin"].cpu().numpy(), cal["cin"])
+    A.close()
+
+
+def test_regions_error_paths(ctx):
+    n_p, nsim = 50, 20
+    M = dev_cm(np.full((n_p, nsim), -3.0))
+    zhat = dev(np.zeros(n_p))
+    v = dev(np.ones(n_p))
+    out = g.excursion_regions(ctx, M, n_p, 0, nsim, 0.0, 0.9, zhat=zhat, v=v)
+    assert out["status"] == g.ERR_EMPTY_SAMPLE and out["n_psi"] == 0
+    assert np.all(out["psi"] == np.inf)
+    v2 = dev(np.r_[np.ones(n_p - 1), 0.0])
+    out = g.excursion_regions(ctx, M, n_p, 0, nsim, -5.0, 0.9, zhat=zhat, v=v2)
+    assert out["status"] == g.ERR_MSPE_NONPOS
