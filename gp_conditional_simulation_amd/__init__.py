@@ -38,7 +38,7 @@ class CovParams(C.Structure):
 
 
 class PrecOpts(C.Structure):
-    _fields_ = [("amp", C.c_int), ("tol", C.c_double), ("allow_fp16", C.c_int), ("nt_rule", C.c_int)]
+    _fields_ = [("amp", C.c_int), ("tol", C.c_double), ("allow_fp16", C.c_int), ("unscaled_rule", C.c_int)]
 
 
 class Diag(C.Structure):
@@ -216,14 +216,14 @@ class Tiled:
 
 
 def cov_gen(ctx: Context, loc, n: int, params: dict, nb: int, amp: int = 0, tol: float = 0.0,
-            allow_fp16: bool = True, nt_rule: bool = False, diag_add=None) -> Tiled:
+            allow_fp16: bool = True, nt_rule: bool = True, diag_add=None) -> Tiled:
     """gpex_cov_gen.  loc: float64 device tensor of 2n values (x then y)."""
     import torch
     _dev_check(loc, ctx, torch.float64)
     _dev_check(diag_add, ctx, torch.float64)
     cp = CovParams(int(params.get("kind", 0)), float(params["sigma2"]), float(params["range"]),
                    float(params.get("nu", 0.5)), float(params.get("nugget", 0.0)))
-    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(nt_rule))
+    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(not nt_rule))
     h = C.c_void_p()
     d = Diag()
     rc = lib().gpex_cov_gen(ctx.h, _ptr(loc), n, _ptr(diag_add), C.byref(cp), nb, C.byref(po), C.byref(h),
@@ -250,13 +250,13 @@ def normals(ctx: Context, seed: int, stream: int, n: int, nsim: int, out=None):
     return out
 
 
-def plan(stats, nt: int, amp: int = 1, tol: float = 0.0, allow_fp16: bool = True, nt_rule: bool = False):
+def plan(stats, nt: int, amp: int = 1, tol: float = 0.0, allow_fp16: bool = True, nt_rule: bool = True):
     """gpex_plan (host only): precision map and diagnostics from tile statistics."""
     st = np.ascontiguousarray(stats, dtype=np.float64).reshape(-1)
     if st.size != 3 * nt * (nt + 1) // 2:
         raise ValueError("stats must hold 3 values per lower tile")
     pmap = np.zeros((nt, nt), dtype=np.uint8)
-    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(nt_rule))
+    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(not nt_rule))
     d = Diag()
     rc = lib().gpex_plan(st.ctypes.data, nt, C.byref(po), pmap.ctypes.data, C.byref(d))
     if rc != 0:

@@ -75,7 +75,7 @@ extern "C" int gpex_ctx_set_timing(gpex_ctx_t ctx, int on) {
 
 extern "C" int gpex_ctx_timings(gpex_ctx_t ctx, double* out) {
     if (!ctx || !out) return GPEX_ERR_ARG;
-    for (int i = 0; i < 16; ++i) out[i] = i < 12 ? ctx->timings[i] : 0.0;
+    for (int i = 0; i < 16; ++i) out[i] = ctx->timings[i];
     return GPEX_OK;
 }
 

@@ -6,9 +6,10 @@
 //   * diagonal tile (k, k): FP64 POTRF.  Here it is factored together with its explicit inverse
 //     T_k = L_kk^-1 by recursive halving down to a single-workgroup 64 x 64 leaf (LDS resident);
 //     the halves are joined with FP64 matrix-core GEMMs.
-//   * panel tiles (i, k), i > k: L_ik = A_ik L_kk^-T evaluated as the product A_ik T_k^T in the
-//     tile's precision (FP64 tiles in FP64, FP32 and FP16 tiles in FP32 with FP16 stored back),
-//     one batched launch per compute precision.
+//   * panel tiles (i, k), i > k: L_ik = A_ik L_kk^-T evaluated as the product A_ik T_k^T on FP64
+//     matrix cores for every tile and rounded once to the tile's storage precision (one batched
+//     launch).  An FP32 product through the explicit inverse carries an error of about
+//     kappa(L_kk) u_32 and, on strongly correlated covariances, costs positive definiteness.
 //   * trailing tiles (i, j), k < j <= i: A_ij -= L_ik L_jk^T in the precision of A_ij with the
 //     operands converted to it (FP16 on FP16 matrix cores with FP32 accumulation), one batched
 //     launch per compute precision; diagonal tiles (the SYRK tasks) are FP64.
@@ -218,7 +219,8 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     };
 
     // Per-step task lists, built once on the host and uploaded in one copy.
-    // Lists per step: 0 panel FP64, 1 panel FP32, 2 update FP64, 3 update FP32, 4 update FP16.
+    // Lists per step: 0 panel solves (FP64 compute), 1 unused, 2 update FP64, 3 update FP32,
+    // 4 update FP16.
     std::vector<GemmTask> tasks;
     std::vector<CopyTask> copies;
     std::vector<int64_t> list_beg((size_t)nt * 5 + 1, 0);
@@ -236,7 +238,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             if (li < 2) {
                 for (int64_t i = k + 1; i < nt; ++i) {
                     int p = a->prec(i, k);
-                    if ((li == 0) != (p == DT_F64)) continue;
+                    if (li == 1) continue;
                     GemmTask g{};
                     g.A = static_cast<uint8_t*>(pws) + 8 * tile_el * (i - k - 1);
                     g.B = a->tinv_tile(k);
@@ -323,7 +325,8 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
                 rc.b = tm.next();
                 (void)hipEventRecord(rc.b, s);
             }
-            POTRF_TRY(gemm_launch(ctx, s, compute, d_tasks + b0, (int)(b1 - b0), tasks[(size_t)b0]));
+            POTRF_TRY(gemm_launch(ctx, s, compute, d_tasks + b0, (int)(b1 - b0), tasks[(size_t)b0],
+                                  li >= 2 ? GEMM_UPDATE : GEMM_GENERIC));
             if (ctx->timing && li >= 2) {
                 rc.e = tm.next();
                 (void)hipEventRecord(rc.e, s);

@@ -25,8 +25,7 @@ struct gpex_ctx_s {
     std::string err;
     long long* d_flags = nullptr;     // FLAG_COUNT device words
     bool timing = false;
-    hipEvent_t ev[8] = {};
-    double timings[6] = {0, 0, 0, 0, 0, 0};
+    double timings[16] = {};          // layout documented at gpex_ctx_timings
 };
 
 struct gpex_tiled_s {
@@ -90,8 +89,9 @@ struct GemmTask {
 // compute: DT_F64 (FP64 matrix cores), DT_F32 (FP32 matrix cores) or DT_F16 (FP16 matrix cores,
 // FP32 accumulation).  Either `d_tasks` (device array of ntasks tasks with identical M, N, K) or,
 // when d_tasks is null, the single task `one` passed by value.
+enum : int { GEMM_GENERIC = 0, GEMM_UPDATE = 1, GEMM_TRMM = 2 };
 int gemm_launch(gpex_ctx_t ctx, hipStream_t s, int compute, const GemmTask* d_tasks, int ntasks,
-                const GemmTask& one);
+                const GemmTask& one, int role = GEMM_GENERIC);
 
 // Convenience: single-task GEMM on the context stream.
 int gemm1(gpex_ctx_t ctx, int compute, const void* A, int ta, int transA, int64_t lda,

@@ -7,8 +7,9 @@
 //              Eq. 11 relative magnitude of the FP16 tiles;
 //   Sec. V-E   Eq. 12: l_f = sqrt(x_min,norm / v_min), u_f = sqrt(x_max / v_max) over present
 //              reduced formats, u_s = min(65504, min_f u_f), s = floor(u_s) - 1 when that exceeds 1.
-// Readings where the page is silent or garbled: the tile rule r * eps_p <= tol with
-// r = ||V_ij||_F / ||V||_F (optionally r * NT * eps_p); Eq. 11 as max(rho1, rho2) < 1e-4/2^-10;
+// Readings where the page is silent or garbled: the tile rule r * NT * eps_p <= tol with
+// r = ||V_ij||_F / ||V||_F and NT tile rows (the unscaled r * eps_p <= tol on request);
+// Eq. 11 as max(rho1, rho2) < 1e-4/2^-10;
 // no FP16 tile -> Eq. 10/11 pass vacuously; no reduced tile -> u_s = 65504.
 // ||V||_F^2 is summed in row-packed tile order, off-diagonal tiles twice.
 #include <cmath>
@@ -32,7 +33,7 @@ void plan_precision(const std::vector<double>& st, int64_t nt, const gpex_prec_o
     for (int64_t i = 0; i < nt; ++i)
         for (int64_t j = 0; j <= i; ++j) f2 += (i == j) ? T(i, j)[0] : 2.0 * T(i, j)[0];
     d.frob = std::sqrt(f2);
-    const double mult = o.nt_rule ? (double)nt : 1.0;
+    const double mult = o.unscaled_rule ? 1.0 : (double)nt;
     for (int64_t i = 0; i < nt; ++i)
         for (int64_t j = 0; j <= i; ++j) {
             uint8_t p = DT_F64;

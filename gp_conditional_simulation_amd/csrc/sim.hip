@@ -300,10 +300,10 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
         g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
         g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
-        r = gemm_launch(ctx, s, amp ? DT_F32 : DT_F64, nullptr, 1, g);
+        r = gemm_launch(ctx, s, amp ? DT_F32 : DT_F64, nullptr, 1, g, GEMM_TRMM);
         if (r >= 0 && beg[(size_t)k + 1] > beg[(size_t)k])
             r = gemm_launch(ctx, s, amp ? DT_F16 : DT_F64, d_tasks + beg[(size_t)k],
-                            (int)(beg[(size_t)k + 1] - beg[(size_t)k]), tasks[(size_t)beg[(size_t)k]]);
+                            (int)(beg[(size_t)k + 1] - beg[(size_t)k]), tasks[(size_t)beg[(size_t)k]], GEMM_TRMM);
         if (r < 0) { cleanup(); return r; }
     }
     if (ctx->timing) (void)hipEventRecord(ev[2], s);

@@ -64,14 +64,14 @@ typedef struct {
 } gpex_cov_params;
 
 /* Precision options.  amp = 0: every tile FP64 and s = 1 (Algorithm 1, AMP = 0 branch).
- * amp = 1: off-diagonal tile (i, j) with r = ||V_ij||_F / ||V||_F goes to FP16 when allow_fp16
- * and r * 2^-10 <= tol, else to FP32 when r * 2^-23 <= tol, else stays FP64 (nt_rule != 0
- * multiplies r by the tile count first).  tol is the pages' fixedacc. */
+ * amp = 1: with r = ||V_ij||_F / ||V||_F and NT tile rows, off-diagonal tile (i, j) goes to FP16
+ * when allow_fp16 and r * NT * 2^-10 <= tol, else to FP32 when r * NT * 2^-23 <= tol, else stays
+ * FP64; unscaled_rule != 0 drops the NT factor (r * eps <= tol).  tol is the pages' fixedacc. */
 typedef struct {
     int amp;
     double tol;
     int allow_fp16;
-    int nt_rule;
+    int unscaled_rule;
 } gpex_prec_opts;
 
 /* Diagnostics of the plan (Sec. V-D, V-E) and of the simulation input (Algorithm 1). */

@@ -8,9 +8,9 @@ Follows "Mixed-Precision GPU Acceleration for Confidence Regions of Spatial Excu
   Sec. V-E    Eq. 12 covariance scale s.
 
 Readings where the pages leave a step open:
-  * rule: tile (i, j), i > j, with r = ||V_ij||_F / ||V||_F goes to FP16 when FP16 is allowed and
-    r * 2^-10 <= tol, else to FP32 when r * 2^-23 <= tol, else FP64 (``nt_rule`` multiplies r by
-    the tile count NT first);
+  * rule: tile (i, j), i > j, with r = ||V_ij||_F / ||V||_F and NT tile rows goes to FP16 when
+    FP16 is allowed and r * NT * 2^-10 <= tol, else to FP32 when r * NT * 2^-23 <= tol, else FP64
+    (``nt_rule=False`` drops the NT factor);
   * Eq. 11 is read as max(rho1, rho2) < 1e-4 / eps_FP16 with eps_FP16 = 2^-10 (the extraction
     prints the fraction's numerator first, as it does for Eq. 10);
   * Eq. 10 with no FP16 tiles passes vacuously; with a non-positive FP16 minimum it fails;
@@ -53,7 +53,7 @@ class PlanResult:
 
 
 def plan(stats: np.ndarray, nt: int, tol: float, amp: int = 1, allow_fp16: bool = True,
-         nt_rule: bool = False) -> PlanResult:
+         nt_rule: bool = True) -> PlanResult:
     stats = np.asarray(stats, dtype=np.float64).reshape(-1, 3)
     assert stats.shape[0] == nt * (nt + 1) // 2
     pmap = np.full((nt, nt), 255, dtype=np.uint8)

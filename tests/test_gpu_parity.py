@@ -80,7 +80,7 @@ def test_plan_from_device_stats_matches_oracle_plan(ctx, tol):
     x, y, params = setup_case(n, nb, 1.5, 0.03, 12)
     A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=tol)
     info = A.info()
-    r = oracle.plan(A.stats(), info["nt"], tol)
+    r = oracle.plan(A.stats(), info["nt"], tol, nt_rule=True)
     low = np.tril_indices(info["nt"])
     assert np.array_equal(info["map"][low], r.pmap[low])
     assert info["s"] == r.s and A.diag["s"] == r.s
@@ -132,20 +132,23 @@ def test_potrf_reports_non_spd(ctx):
 
 
 MP_CASES = [
-    # (n, nb, nu, beta, seed, tol)
-    (3200, 320, 1.5, 0.03, 1002, 1e-9),
-    (3200, 320, 1.5, 0.1, 1002, 1e-9),
-    (3200, 320, 1.5, 0.3, 1002, 1e-9),
-    (4000, 512, 2.5, 0.1, 1003, 1e-6),
-    (4000, 512, 2.5, 0.1, 1003, 1e-8),
+    # (n, nb, nu, beta, seed, tol, tile-count-scaled rule)
+    (3200, 320, 1.5, 0.03, 1002, 1e-9, False),
+    (3200, 320, 1.5, 0.1, 1002, 1e-9, False),
+    (3200, 320, 1.5, 0.3, 1002, 1e-7, False),
+    (4000, 512, 2.5, 0.1, 1003, 1e-6, False),
+    (4000, 512, 2.5, 0.1, 1003, 1e-8, False),
+    (4000, 512, 2.5, 0.1, 1003, 1e-6, True),
+    (3200, 320, 1.5, 0.03, 1002, 1e-7, True),
 ]
 
 
-@pytest.mark.parametrize("case", MP_CASES, ids=lambda c: f"n{c[0]}_b{c[3]}_tol{c[5]:g}")
+@pytest.mark.parametrize("case", MP_CASES, ids=lambda c: f"n{c[0]}_b{c[3]}_tol{c[5]:g}_{'nt' if c[6] else 'plain'}")
 def test_potrf_and_trmm_mixed_precision(ctx, case):
-    n, nb, nu, beta, seed, tol = case
+    n, nb, nu, beta, seed, tol, nt_rule = case
     x, y, params = setup_case(n, nb, nu, beta, seed)
-    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=tol)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=tol, nt_rule=nt_rule)
+    assert A.diag["tiles"][1] + A.diag["tiles"][2] > 0, "case must exercise reduced-precision tiles"
     assert g.potrf_mp(ctx, A) == 0
     L = A.to_dense().cpu().numpy()
     V = oracle.cov_matrix(x, y, 0, 1.0, beta, nu, nugget=1e-4)
@@ -168,10 +171,10 @@ def test_loose_tolerance_reports_failed_checks(ctx):
     # tolerance, the failure is reported (Sec. V-D) while the factorisation still runs
     n, nb = 2000, 160
     x, y, params = setup_case(n, nb, 1.5, 0.03, 9)
-    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=1e-4)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=1e-4, nt_rule=False)
     assert A.status == g.WARN_CHECKS_FAILED
     assert not A.diag["eq11_pass"]
-    r = oracle.plan(A.stats(), A.info()["nt"], 1e-4)
+    r = oracle.plan(A.stats(), A.info()["nt"], 1e-4, nt_rule=False)
     assert not r.eq11_pass and A.diag["tiles"] == list(r.tiles)
     assert g.potrf_mp(ctx, A) >= 0
     A.close()

@@ -395,6 +395,17 @@ def test_planner_worked_example():
     assert list(r.tiles) == g["tiles"]
 
 
+def test_planner_rule_variants_worked_example():
+    g = _gold("planner_worked_example.json")
+    rc = g["rule_cases"]
+    st = np.array(g["stats"])
+    ru = oracle.plan(st, g["nt"], rc["tol"], nt_rule=False)
+    rs = oracle.plan(st, g["nt"], rc["tol"], nt_rule=True)
+    for i in range(g["nt"]):
+        assert ru.pmap[i, :i + 1].tolist() == rc["unscaled_pmap_lower"][i]
+        assert rs.pmap[i, :i + 1].tolist() == rc["scaled_pmap_lower"][i]
+
+
 def test_planner_edge_cases():
     st = np.array([[100.0, 0.5, 1.0], [50.0, 0.2, 0.9], [100.0, 0.5, 1.0]])
     r0 = oracle.plan(st, 2, 1e-8, amp=0)
