@@ -16,6 +16,7 @@
 // The T_k are kept in the handle: kriging reuses them for its blocked triangular solves.
 #include <algorithm>
 #include <cmath>
+#include <map>
 
 #include "common.h"
 #include "devutil.h"
@@ -218,14 +219,20 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         dev_free(ws);
     };
 
-    // Per-step task lists, built once on the host and uploaded in one copy.
-    // Lists per step: 0 panel solves (FP64 compute), 1 unused, 2 update FP64, 3 update FP32,
-    // 4 update FP16.
+    // Per-step task groups, built once on the host and uploaded in one copy.  A group holds the
+    // tasks of one step with one compute precision and one operand-type signature (a launch runs
+    // one typed kernel).  Panel solves: FP64 compute for every tile; updates: the output tile's
+    // precision.
+    struct Group { int64_t b0, b1; int compute, role, k; };
     std::vector<GemmTask> tasks;
     std::vector<CopyTask> copies;
-    std::vector<int64_t> list_beg((size_t)nt * 5 + 1, 0);
+    std::vector<Group> groups;
+    std::vector<int64_t> group_beg((size_t)nt + 1, 0);
     std::vector<int64_t> copy_beg((size_t)nt + 1, 0);
     std::vector<double> upd_flops(3, 0.0);
+    auto sig = [](int compute, const GemmTask& g) {
+        return compute * 1000 + g.ta * 100 + g.tb * 10 + g.tc;
+    };
     for (int64_t k = 0; k < nt; ++k) {
         for (int64_t i = k + 1; i < nt; ++i) {
             CopyTask c{a->tile(i, k), static_cast<uint8_t*>(pws) + 8 * tile_el * (i - k - 1),
@@ -233,45 +240,48 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             copies.push_back(c);
         }
         copy_beg[(size_t)k + 1] = (int64_t)copies.size();
-        for (int li = 0; li < 5; ++li) {
-            list_beg[(size_t)k * 5 + li] = (int64_t)tasks.size();
-            if (li < 2) {
-                for (int64_t i = k + 1; i < nt; ++i) {
-                    int p = a->prec(i, k);
-                    if (li == 1) continue;
-                    GemmTask g{};
-                    g.A = static_cast<uint8_t*>(pws) + 8 * tile_el * (i - k - 1);
-                    g.B = a->tinv_tile(k);
-                    g.C = a->tile(i, k);
-                    g.lda = g.ldb = g.ldc = nb;
-                    g.M = g.N = g.K = nb;
-                    g.ta = (int8_t)p; g.tb = DT_F64; g.tc = (int8_t)p;
-                    g.transA = 0; g.transB = 1;
-                    g.alpha = 1.0; g.beta = 0.0;
-                    tasks.push_back(g);
-                }
-            } else {
-                int want = li - 2;
-                for (int64_t j = k + 1; j < nt; ++j)
-                    for (int64_t i = j; i < nt; ++i) {
-                        int p = (i == j) ? DT_F64 : a->prec(i, j);
-                        if (p != want) continue;
-                        GemmTask g{};
-                        g.A = a->tile(i, k);
-                        g.B = a->tile(j, k);
-                        g.C = a->tile(i, j);
-                        g.lda = g.ldb = g.ldc = nb;
-                        g.M = g.N = g.K = nb;
-                        g.ta = (int8_t)a->prec(i, k); g.tb = (int8_t)a->prec(j, k); g.tc = (int8_t)p;
-                        g.transA = 0; g.transB = 1;
-                        g.alpha = -1.0; g.beta = 1.0;
-                        tasks.push_back(g);
-                        upd_flops[want] += (i == j ? 1.0 : 2.0) * nb * (double)nb * nb;
-                    }
+        group_beg[(size_t)k] = (int64_t)groups.size();
+        std::map<int, std::vector<GemmTask>> panel, update;
+        for (int64_t i = k + 1; i < nt; ++i) {
+            int p = a->prec(i, k);
+            GemmTask g{};
+            g.A = static_cast<uint8_t*>(pws) + 8 * tile_el * (i - k - 1);
+            g.B = a->tinv_tile(k);
+            g.C = a->tile(i, k);
+            g.lda = g.ldb = g.ldc = nb;
+            g.M = g.N = g.K = nb;
+            g.ta = (int8_t)p; g.tb = DT_F64; g.tc = (int8_t)p;
+            g.transA = 0; g.transB = 1;
+            g.alpha = 1.0; g.beta = 0.0;
+            panel[sig(DT_F64, g)].push_back(g);
+        }
+        for (int64_t j = k + 1; j < nt; ++j)
+            for (int64_t i = j; i < nt; ++i) {
+                int p = (i == j) ? DT_F64 : a->prec(i, j);
+                GemmTask g{};
+                g.A = a->tile(i, k);
+                g.B = a->tile(j, k);
+                g.C = a->tile(i, j);
+                g.lda = g.ldb = g.ldc = nb;
+                g.M = g.N = g.K = nb;
+                g.ta = (int8_t)a->prec(i, k); g.tb = (int8_t)a->prec(j, k); g.tc = (int8_t)p;
+                g.transA = 0; g.transB = 1;
+                g.alpha = -1.0; g.beta = 1.0;
+                update[sig(p, g)].push_back(g);
+                upd_flops[(size_t)p] += (i == j ? 1.0 : 2.0) * nb * (double)nb * nb;
             }
+        for (auto& kv : panel) {
+            groups.push_back(Group{(int64_t)tasks.size(), 0, DT_F64, GEMM_GENERIC, (int)k});
+            tasks.insert(tasks.end(), kv.second.begin(), kv.second.end());
+            groups.back().b1 = (int64_t)tasks.size();
+        }
+        for (auto& kv : update) {
+            groups.push_back(Group{(int64_t)tasks.size(), 0, kv.first / 1000, GEMM_UPDATE, (int)k});
+            tasks.insert(tasks.end(), kv.second.begin(), kv.second.end());
+            groups.back().b1 = (int64_t)tasks.size();
         }
     }
-    list_beg[(size_t)nt * 5] = (int64_t)tasks.size();
+    group_beg[(size_t)nt] = (int64_t)groups.size();
     GemmTask* d_tasks = nullptr;
     CopyTask* d_copies = nullptr;
     if (!tasks.empty()) {
@@ -295,8 +305,8 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         if (r_ < 0) { cleanup_all(); return r_; } \
     } while (0)
 
-    POTRF_TRY(hipMemsetAsync(ctx->d_flags + FLAG_INFO, 0, sizeof(long long), s) == hipSuccess
-                  ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "memset info"));
+    POTRF_TRY(hipMemsetAsync(ctx->d_flags + FLAG_INFO, 0, sizeof(long long) * (FLAG_BADTASK + 1), s) == hipSuccess
+                  ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "memset flags"));
     Timer tm{ctx};
     struct Rec { hipEvent_t b, e; int prec; };
     std::vector<Rec> recs;
@@ -316,18 +326,16 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             hipLaunchKernelGGL(k_copy_tasks, grid, dim3(256), 0, s, d_copies + copy_beg[(size_t)k], chunk);
             POTRF_TRY(hipGetLastError() == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "panel copy launch"));
         }
-        for (int li = 0; li < 5; ++li) {
-            int64_t b0 = list_beg[(size_t)k * 5 + li], b1 = list_beg[(size_t)k * 5 + li + 1];
-            if (b1 <= b0) continue;
-            int compute = li == 0 ? DT_F64 : li == 1 ? DT_F32 : li - 2;
-            Rec rc{nullptr, nullptr, li - 2};
-            if (ctx->timing && li >= 2) {
+        for (int64_t gi = group_beg[(size_t)k]; gi < group_beg[(size_t)k + 1]; ++gi) {
+            const Group& G = groups[(size_t)gi];
+            const bool upd = G.role == GEMM_UPDATE;
+            Rec rc{nullptr, nullptr, G.compute};
+            if (ctx->timing && upd) {
                 rc.b = tm.next();
                 (void)hipEventRecord(rc.b, s);
             }
-            POTRF_TRY(gemm_launch(ctx, s, compute, d_tasks + b0, (int)(b1 - b0), tasks[(size_t)b0],
-                                  li >= 2 ? GEMM_UPDATE : GEMM_GENERIC));
-            if (ctx->timing && li >= 2) {
+            POTRF_TRY(gemm_launch(ctx, s, G.compute, d_tasks + G.b0, (int)(G.b1 - G.b0), tasks[(size_t)G.b0], G.role));
+            if (ctx->timing && upd) {
                 rc.e = tm.next();
                 (void)hipEventRecord(rc.e, s);
                 recs.push_back(rc);
@@ -359,9 +367,11 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             ctx->timings[2 + 3 * rc.prec] += 1;
         }
     }
-    long long fl = 0;
+    long long fl = 0, bad = 0;
     (void)hipMemcpy(&fl, ctx->d_flags + FLAG_INFO, sizeof(long long), hipMemcpyDeviceToHost);
+    (void)hipMemcpy(&bad, ctx->d_flags + FLAG_BADTASK, sizeof(long long), hipMemcpyDeviceToHost);
     cleanup_all();
+    if (bad) return set_err(ctx, GPEX_ERR_STATE, "gpex_potrf_mp: internal task-type mismatch");
     *info = fl;
     a->factored = true;
     if (fl != 0) {

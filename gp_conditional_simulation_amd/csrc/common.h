@@ -15,7 +15,7 @@ enum : int { DT_F64 = 0, DT_F32 = 1, DT_F16 = 2 };
 inline size_t dt_size(int dt) { return dt == DT_F64 ? 8 : (dt == DT_F32 ? 4 : 2); }
 
 // Device-side flag words kept per context (zeroed by the entry points that use them).
-enum : int { FLAG_INFO = 0, FLAG_FP16_OVF = 1, FLAG_MSPE = 2, FLAG_COUNT = 4 };
+enum : int { FLAG_INFO = 0, FLAG_FP16_OVF = 1, FLAG_MSPE = 2, FLAG_BADTASK = 3, FLAG_COUNT = 4 };
 
 }  // namespace gpex
 
@@ -87,8 +87,10 @@ struct GemmTask {
 };
 
 // compute: DT_F64 (FP64 matrix cores), DT_F32 (FP32 matrix cores) or DT_F16 (FP16 matrix cores,
-// FP32 accumulation).  Either `d_tasks` (device array of ntasks tasks with identical M, N, K) or,
-// when d_tasks is null, the single task `one` passed by value.
+// FP32 accumulation).  Either `d_tasks` (device array of ntasks tasks with identical M, N, K,
+// element types and layout flags, those of `one`) or, when d_tasks is null, the single task
+// `one` passed by value.  A task whose types differ from `one`'s sets flags[FLAG_BADTASK] and
+// is skipped.
 enum : int { GEMM_GENERIC = 0, GEMM_UPDATE = 1, GEMM_TRMM = 2 };
 int gemm_launch(gpex_ctx_t ctx, hipStream_t s, int compute, const GemmTask* d_tasks, int ntasks,
                 const GemmTask& one, int role = GEMM_GENERIC);

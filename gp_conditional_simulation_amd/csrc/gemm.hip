@@ -271,6 +271,254 @@ __global__ __launch_bounds__(NTHR) void k_gemm(const GemmTask* __restrict__ task
     if (ovf && flags) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Typed kernel: operand element types fixed at compile time (the hot launches: trailing updates
+// and TRMM with uniform operand types), global-address-space operand pointers, K slabs of 32
+// (FP64/FP32) or 64 (FP16) staged through two LDS buffers, one barrier per slab.
+template <typename T> struct DtOf;
+template <> struct DtOf<double> { static constexpr int v = DT_F64; };
+template <> struct DtOf<float> { static constexpr int v = DT_F32; };
+template <> struct DtOf<_Float16> { static constexpr int v = DT_F16; };
+
+template <typename T> using gptr = const __attribute__((address_space(1))) T*;
+template <typename T> using gptr_mut = __attribute__((address_space(1))) T*;
+
+template <typename CT> struct TCfg;
+template <> struct TCfg<double> { static constexpr int BK = 16, PAD = 2, KSTEP = 4; };
+template <> struct TCfg<float> { static constexpr int BK = 32, PAD = 4, KSTEP = 4; };
+template <> struct TCfg<_Float16> { static constexpr int BK = 64, PAD = 8, KSTEP = 32; };
+
+template <typename CT, typename T> __device__ __forceinline__ CT to_ct(T v);
+template <> __device__ __forceinline__ double to_ct<double, double>(double v) { return v; }
+template <> __device__ __forceinline__ double to_ct<double, float>(float v) { return (double)v; }
+template <> __device__ __forceinline__ double to_ct<double, _Float16>(_Float16 v) { return (double)v; }
+template <> __device__ __forceinline__ float to_ct<float, double>(double v) { return (float)v; }
+template <> __device__ __forceinline__ float to_ct<float, float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_ct<float, _Float16>(_Float16 v) { return (float)v; }
+template <> __device__ __forceinline__ _Float16 to_ct<_Float16, double>(double v) { return f64_to_f16(v); }
+template <> __device__ __forceinline__ _Float16 to_ct<_Float16, float>(float v) { return (_Float16)v; }
+template <> __device__ __forceinline__ _Float16 to_ct<_Float16, _Float16>(_Float16 v) { return v; }
+
+template <typename T> struct V4;
+template <> struct V4<double> { typedef double __attribute__((ext_vector_type(4))) type; };
+template <> struct V4<float> { typedef float __attribute__((ext_vector_type(4))) type; };
+template <> struct V4<_Float16> { typedef _Float16 __attribute__((ext_vector_type(4))) type; };
+
+// One operand slab (128 rows x BK) of the typed kernel.  CR: the row index is contiguous in
+// global memory.  LDS layout: FP64/FP32 operands with CR are kept as [k][row] (row stride LDR,
+// padded so that the four lane groups of a fragment read hit different banks; stores are plain
+// vector writes); all other operands as [row][k] (k contiguous, the FP16 fragments need 8
+// consecutive k per lane).
+template <typename CT, typename T, bool CR, bool EDGE>
+struct TSlab {
+    static constexpr int BK = TCfg<CT>::BK;
+    static constexpr bool KROW = CR && sizeof(CT) >= 4;        // [k][row] layout
+    static constexpr int LDK = BK + TCfg<CT>::PAD;               // [row][k] row stride
+    static constexpr int LDR = 128 + (sizeof(CT) == 8 ? 4 : 8);  // [k][row] k stride
+    static constexpr int ELEMS = KROW ? BK * LDR : 128 * LDK;
+    static constexpr int VPT = (128 * BK / NTHR) / 4;
+    CT v[VPT][4];
+
+    __device__ __forceinline__ static int idx(int row, int k) { return KROW ? k * LDR + row : row * LDK + k; }
+
+    __device__ __forceinline__ void load(gptr<T> base, int64_t ld, int r0, int k0, int R, int K, int t) {
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) {
+            int r, k;
+            if (CR) {
+                r = (t % 32) * 4;
+                k = t / 32 + 8 * q;
+            } else {
+                constexpr int TPR = BK / 4;
+                r = t / TPR + (NTHR / TPR) * q;
+                k = (t % TPR) * 4;
+            }
+            int gr = r0 + r, gk = k0 + k;
+            if (!EDGE) {
+                int64_t id = CR ? (int64_t)gr + (int64_t)gk * ld : (int64_t)gk + (int64_t)gr * ld;
+                typename V4<T>::type x = *reinterpret_cast<const __attribute__((address_space(1))) typename V4<T>::type*>(base + id);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[q][e] = to_ct<CT, T>(x[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    int rr = CR ? gr + e : gr;
+                    int kk = CR ? gk : gk + e;
+                    v[q][e] = (rr < R && kk < K)
+                                  ? to_ct<CT, T>(base[CR ? (int64_t)rr + (int64_t)kk * ld : (int64_t)kk + (int64_t)rr * ld])
+                                  : CT(0);
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ void store(CT* sm, int t) {
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) {
+            if (CR) {
+                int r = (t % 32) * 4, k = t / 32 + 8 * q;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm[idx(r + e, k)] = v[q][e];
+            } else {
+                constexpr int TPR = BK / 4;
+                int r = t / TPR + (NTHR / TPR) * q, k = (t % TPR) * 4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm[idx(r, k + e)] = v[q][e];
+            }
+        }
+    }
+};
+
+template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, bool EDGE, int ROLE>
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int bmc, int bnc, int xcd_map,
+              unsigned long long* flags) {
+    constexpr int BK = TCfg<CT>::BK;
+    constexpr bool a_contig_r = TRA == 0;
+    constexpr bool b_contig_r = TRB != 0;
+    typedef TSlab<CT, TA, a_contig_r, EDGE> SA;
+    typedef TSlab<CT, TB, b_contig_r, EDGE> SB;
+    __shared__ __attribute__((aligned(16))) CT As[2][SA::ELEMS];
+    __shared__ __attribute__((aligned(16))) CT Bs[2][SB::ELEMS];
+
+    const int bpt = bmc * bnc;
+    int64_t b = blockIdx.x;
+    int task, blk;
+    if (xcd_map) {
+        int x = (int)(b % 8);
+        int64_t slot = b / 8;
+        task = x + 8 * (int)(slot / bpt);
+        blk = (int)(slot % bpt);
+        if (task >= ntasks) return;
+    } else {
+        task = (int)(b / bpt);
+        blk = (int)(b % bpt);
+    }
+    const GemmTask T = tasks ? tasks[task] : one;
+    if (T.ta != DtOf<TA>::v || T.tb != DtOf<TB>::v || T.tc != DtOf<TC>::v || T.transA != TRA ||
+        (T.transB != 0) != (TRB != 0)) {
+        if (threadIdx.x == 0 && flags) atomicOr(&flags[FLAG_BADTASK], 1ull);
+        return;
+    }
+    gptr<TA> Ap = (gptr<TA>)T.A;
+    gptr<TB> Bp = (gptr<TB>)T.B;
+    gptr_mut<TC> Cp = (gptr_mut<TC>)T.C;
+    const int m0 = (blk % bmc) * BM, n0 = (blk / bmc) * BN;
+    const int t = threadIdx.x, l = t % 64, w = t / 64;
+    const int wm = w / 2, wn = w % 2;
+    typedef typename AccT<CT>::type Acc;
+    Acc acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+    SA la;
+    SB lb;
+    const int nk = (T.K + BK - 1) / BK;
+    la.load(Ap, T.lda, m0, 0, T.M, T.K, t);
+    lb.load(Bp, T.ldb, n0, 0, T.N, T.K, t);
+    la.store(As[0], t);
+    lb.store(Bs[0], t);
+    __syncthreads();
+    for (int kb = 0; kb < nk; ++kb) {
+        const int cur = kb & 1;
+        if (kb + 1 < nk) {
+            la.load(Ap, T.lda, m0, (kb + 1) * BK, T.M, T.K, t);
+            lb.load(Bp, T.ldb, n0, (kb + 1) * BK, T.N, T.K, t);
+        }
+        const CT* as = As[cur];
+        const CT* bs = Bs[cur];
+        if constexpr (sizeof(CT) == 2) {
+#pragma unroll
+            for (int ks = 0; ks < BK; ks += 32) {
+                h8 af[4], bf[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    af[i] = *reinterpret_cast<const h8*>(&as[SA::idx(wm * 64 + i * 16 + l % 16, ks + 8 * (l / 16))]);
+                    bf[i] = *reinterpret_cast<const h8*>(&bs[SB::idx(wn * 64 + i * 16 + l % 16, ks + 8 * (l / 16))]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) mma(acc[i][j], af[i], bf[j]);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < BK; ks += 16) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    CT af[4], bf[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        af[i] = as[SA::idx(wm * 64 + i * 16 + l % 16, ks + 4 * (l / 16) + e)];
+                        bf[i] = bs[SB::idx(wn * 64 + i * 16 + l % 16, ks + 4 * (l / 16) + e)];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) mma(acc[i][j], af[i], bf[j]);
+                }
+            }
+        }
+        if (kb + 1 < nk) {
+            la.store(As[cur ^ 1], t);
+            lb.store(Bs[cur ^ 1], t);
+        }
+        __syncthreads();
+    }
+
+    bool ovf = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                int row = m0 + wm * 64 + i * 16 + acc_row<CT>(l, r);
+                int col = n0 + wn * 64 + j * 16 + l % 16;
+                if (EDGE && (row >= T.M || col >= T.N)) continue;
+                int64_t ci = (int64_t)row + (int64_t)col * T.ldc;
+                if constexpr (sizeof(TC) == 8) {
+                    double v = T.alpha * (double)acc[i][j][r];
+                    if (T.beta != 0.0) v += T.beta * (double)Cp[ci];
+                    Cp[ci] = v;
+                } else if constexpr (sizeof(TC) == 4) {
+                    float v = (float)T.alpha * (float)acc[i][j][r];
+                    if (T.beta != 0.0) v += (float)T.beta * (float)Cp[ci];
+                    Cp[ci] = v;
+                } else if constexpr (sizeof(CT) == 8) {
+                    double v = T.alpha * acc[i][j][r];
+                    if (T.beta != 0.0) v += T.beta * (double)Cp[ci];
+                    _Float16 h = f64_to_f16(v);
+                    if (__builtin_isinf((float)h) && !__builtin_isinf(v)) ovf = true;
+                    Cp[ci] = h;
+                } else {
+                    float v = (float)T.alpha * (float)acc[i][j][r];
+                    if (T.beta != 0.0) v += (float)T.beta * (float)Cp[ci];
+                    _Float16 h = (_Float16)v;
+                    if (__builtin_isinf((float)h) && !__builtin_isinf(v)) ovf = true;
+                    Cp[ci] = h;
+                }
+            }
+    if (ovf && flags) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
+}
+
+// Launch the typed kernel when (ta, tb, tc, transA, transB) match; returns 1 if launched.
+template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, int ROLE>
+static int try_typed(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one,
+                     bool fast, int64_t grid, int bmc, int bnc, int xcd, unsigned long long* fl) {
+    if (one.ta != DtOf<TA>::v || one.tb != DtOf<TB>::v || one.tc != DtOf<TC>::v) return 0;
+    if (one.transA != TRA || (one.transB != 0) != (TRB != 0)) return 0;
+    if (fast)
+        hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE>), dim3((unsigned)grid), dim3(NTHR), 0, s,
+                           d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+    else
+        hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, true, ROLE>), dim3((unsigned)grid), dim3(NTHR), 0, s,
+                           d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+    return 1;
+}
+
 template <typename CT, int ROLE>
 static int launch_ct(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int ntasks,
                      const GemmTask& one) {
@@ -288,6 +536,28 @@ static int launch_ct(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
     int64_t grid = xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt : (int64_t)ntasks * bpt;
     if (grid > 0x7fffffffLL) return set_err(ctx, GPEX_ERR_ARG, "gemm grid too large");
     unsigned long long* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
+    // typed fast kernels for the operand-type combinations of the hot launches
+    bool tfast = (M % BM == 0) && (N % BN == 0) && (K % TCfg<CT>::BK == 0) && (one.lda % 4 == 0) &&
+                 (one.ldb % 4 == 0) && al(one.A) && al(one.B);
+    // NT form (trailing updates, panel solves) and NN form (TRMM) with uniform or TRMM/TRSM types
+    int done = try_typed<CT, CT, CT, CT, 0, 1, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
+    if (!done) done = try_typed<CT, CT, CT, CT, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
+    if constexpr (sizeof(CT) == 2) {
+        if (!done) done = try_typed<CT, double, _Float16, double, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
+        if (!done) done = try_typed<CT, float, _Float16, double, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
+        if (!done) done = try_typed<CT, _Float16, _Float16, double, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
+    }
+    if constexpr (sizeof(CT) == 4) {
+        if (!done) done = try_typed<CT, double, _Float16, double, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
+    }
+    if constexpr (sizeof(CT) == 8) {
+        if (!done) done = try_typed<CT, float, double, float, 0, 1, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
+        if (!done) done = try_typed<CT, _Float16, double, _Float16, 0, 1, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
+    }
+    if (done) {
+        GPEX_HIP(ctx, hipGetLastError());
+        return GPEX_OK;
+    }
     if (fast)
         hipLaunchKernelGGL((k_gemm<CT, false, ROLE>), dim3((unsigned)grid), dim3(NTHR), 0, s, d_tasks, one,
                            ntasks, bmc, bnc, xcd, fl);

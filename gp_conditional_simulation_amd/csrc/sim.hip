@@ -259,28 +259,38 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     int r = dev_alloc(ctx, &B, (size_t)rows * cols * (amp ? 2 : 8), "simulation input B");
     if (r >= 0) r = dev_alloc(ctx, (void**)&Mp, sizeof(double) * rows * cols, "padded M");
     if (r >= 0) r = dev_alloc(ctx, (void**)&part, sizeof(double) * nblkB, "norm partials");
-    // off-diagonal tasks for every step, built once
+    // off-diagonal tasks for every step, built once and grouped by the factor tile's storage type
+    // (one typed kernel per launch)
+    struct Group { int64_t b0, b1; };
     std::vector<GemmTask> tasks;
-    std::vector<int64_t> beg((size_t)nt + 1, 0);
+    std::vector<Group> groups;
+    std::vector<int64_t> gbeg((size_t)nt + 1, 0);
     for (int64_t k = 0; k < nt; ++k) {
-        beg[(size_t)k] = (int64_t)tasks.size();
-        for (int64_t i = k + 1; i < nt; ++i) {
-            GemmTask g{};
-            g.A = L->tile(i, k); g.ta = (int8_t)L->prec(i, k); g.lda = nb; g.transA = 0;
-            g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
-            g.ldb = rows; g.transB = 0;
-            g.C = Mp + i * nb; g.tc = DT_F64; g.ldc = rows;
-            g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
-            g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
-            tasks.push_back(g);
+        gbeg[(size_t)k] = (int64_t)groups.size();
+        for (int ta = DT_F64; ta <= DT_F16; ++ta) {
+            int64_t b0 = (int64_t)tasks.size();
+            for (int64_t i = k + 1; i < nt; ++i) {
+                if (L->prec(i, k) != ta) continue;
+                GemmTask g{};
+                g.A = L->tile(i, k); g.ta = (int8_t)ta; g.lda = nb; g.transA = 0;
+                g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
+                g.ldb = rows; g.transB = 0;
+                g.C = Mp + i * nb; g.tc = DT_F64; g.ldc = rows;
+                g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
+                g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
+                tasks.push_back(g);
+            }
+            if ((int64_t)tasks.size() > b0) groups.push_back(Group{b0, (int64_t)tasks.size()});
         }
     }
-    beg[(size_t)nt] = (int64_t)tasks.size();
+    gbeg[(size_t)nt] = (int64_t)groups.size();
     if (r >= 0 && !tasks.empty()) {
         r = dev_alloc(ctx, (void**)&d_tasks, sizeof(GemmTask) * tasks.size(), "trmm tasks");
         if (r >= 0 && hipMemcpy(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice) != hipSuccess)
             r = set_err(ctx, GPEX_ERR_HIP, "trmm task upload");
     }
+    if (r >= 0 && hipMemsetAsync(ctx->d_flags + FLAG_BADTASK, 0, sizeof(long long), s) != hipSuccess)
+        r = set_err(ctx, GPEX_ERR_HIP, "trmm flag reset");
     if (r < 0) { cleanup(); return r; }
     hipEvent_t ev[4] = {};
     std::vector<hipEvent_t> kev;
@@ -301,18 +311,22 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
         g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
         r = gemm_launch(ctx, s, amp ? DT_F32 : DT_F64, nullptr, 1, g, GEMM_TRMM);
-        if (r >= 0 && beg[(size_t)k + 1] > beg[(size_t)k])
-            r = gemm_launch(ctx, s, amp ? DT_F16 : DT_F64, d_tasks + beg[(size_t)k],
-                            (int)(beg[(size_t)k + 1] - beg[(size_t)k]), tasks[(size_t)beg[(size_t)k]], GEMM_TRMM);
+        for (int64_t gi = gbeg[(size_t)k]; r >= 0 && gi < gbeg[(size_t)k + 1]; ++gi) {
+            const Group& G = groups[(size_t)gi];
+            r = gemm_launch(ctx, s, amp ? DT_F16 : DT_F64, d_tasks + G.b0, (int)(G.b1 - G.b0), tasks[(size_t)G.b0],
+                            GEMM_TRMM);
+        }
         if (r < 0) { cleanup(); return r; }
     }
     if (ctx->timing) (void)hipEventRecord(ev[2], s);
     r = copy2d(ctx, s, Mp, DT_F64, rows, d_M, DT_F64, ldm, n, nsim, 1.0);
     if (ctx->timing) (void)hipEventRecord(ev[3], s);
     if (r < 0) { cleanup(); return r; }
+    long long bad = 0;
     if (diag || ctx->timing) {
         std::vector<double> h((size_t)nblkB);
         hipError_t e = hipMemcpyAsync(h.data(), part, sizeof(double) * nblkB, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipMemcpyAsync(&bad, ctx->d_flags + FLAG_BADTASK, sizeof(long long), hipMemcpyDeviceToHost, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "trmm sync"); }
         double ss = 0.0;
@@ -331,9 +345,12 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         }
     } else {
         // buffers are freed below; make sure the queued work no longer needs them
-        if (hipStreamSynchronize(s) != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "trmm sync"); }
+        hipError_t e = hipMemcpyAsync(&bad, ctx->d_flags + FLAG_BADTASK, sizeof(long long), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "trmm sync"); }
     }
     cleanup();
+    if (bad) return set_err(ctx, GPEX_ERR_STATE, "gpex_trmm_sim: internal task-type mismatch");
     return GPEX_OK;
 }
 
