@@ -57,6 +57,20 @@ def tile_flops(pmap, nt, nb, nsim, amp):
     return f
 
 
+def traffic_per_launch(prec):
+    """HBM bytes per trailing-update launch from the committed counter summary, if it was taken
+    on the current GEMM source (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"potrf_update_{prec}_unif100k_traffic.json")
+    src = os.path.join(ROOT, "gp_conditional_simulation_amd", "csrc", "gemm.hip")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
 def cpu_baseline(w, rows):
     """Oracle (plain C, FP64, OpenMP) on the leading rows x rows block with all nsim columns."""
     import oracle
@@ -86,8 +100,10 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="unif100k_tol1e-8")
-    ap.add_argument("--cpu-rows", type=int, default=6144)
+    ap.add_argument("--cpu-rows", type=int, default=10240)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library's path is single-device (use --gpus 1)",
@@ -110,6 +126,12 @@ def main():
     ctx = g.Context(0)
     ctx.set_timing(True)
     M = g.colmajor(w.n, w.nsim, ctx)
+    if args.copy_calibration_mib:
+        src = torch.ones(args.copy_calibration_mib * 2 ** 20 // 8, dtype=torch.float64, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)          # reads and writes exactly copy_calibration_mib MiB
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
 
     def step():
@@ -184,9 +206,9 @@ def main():
                                         "frac": round(t_ideal / ((T_potrf + T_trmm) * 1e-3), 4),
                                         "flops": {k: float(f"{v:.4e}") for k, v in tf.items()}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TF[prec], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TF[prec], 4), "traffic": None,
-                     "kernel": f"gpex::k_gemm<{ {'fp64': 'double', 'fp32': 'float', 'fp16': '_Float16'}[prec]}, false, 1> "
-                               f"(trailing tile update, {prec})",
+                     "frac": round(achieved / PEAK_TF[prec], 4), "traffic": traffic_per_launch(prec),
+                     "kernel": "gpex::k_gemm_t<{0}, {0}, {0}, {0}, 0, 1, false, 1> (trailing tile update, {1})".format(
+                         {"fp64": "double", "fp32": "float", "fp16": "_Float16"}[prec], prec),
                      "launches": launches, "avg_launch_ms": round(per_launch_ms, 4),
                      "flops_per_launch": float(f"{per_launch_flops:.4e}")},
         "counts_sum": last["counts_sum"],
