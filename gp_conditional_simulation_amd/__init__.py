@@ -27,7 +27,7 @@ ERR_NOT_SPD, ERR_MSPE_NONPOS, ERR_EMPTY_SAMPLE, WARN_CHECKS_FAILED, WARN_FP16_OV
 STATUS_NAMES = {0: "OK", -1: "ERR_ARG", -2: "ERR_HIP", -3: "ERR_NOMEM", -4: "ERR_STATE", 1: "ERR_NOT_SPD",
                 2: "ERR_MSPE_NONPOS", 3: "ERR_EMPTY_SAMPLE", 4: "WARN_CHECKS_FAILED", 5: "WARN_FP16_OVERFLOW"}
 EXPORTS = ["gpex_version", "gpex_ctx_create", "gpex_ctx_destroy", "gpex_last_error", "gpex_cov_gen",
-           "gpex_tiled_info", "gpex_tiled_stats", "gpex_tiled_to_dense", "gpex_tiled_destroy",
+           "gpex_tiled_info", "gpex_tiled_stats", "gpex_tiled_to_dense", "gpex_tiled_block", "gpex_tiled_destroy",
            "gpex_potrf_mp", "gpex_normals", "gpex_trmm_sim", "gpex_krige", "gpex_excursion_regions",
            "gpex_plan", "gpex_ctx_set_timing", "gpex_ctx_timings"]
 
@@ -85,6 +85,7 @@ def lib():
         L.gpex_tiled_info.argtypes = [P, C.POINTER(I64), C.POINTER(I), C.POINTER(I64), P, C.POINTER(D)]
         L.gpex_tiled_stats.argtypes = [P, P]
         L.gpex_tiled_to_dense.argtypes = [P, P, P, I64]
+        L.gpex_tiled_block.argtypes = [P, P, I64, I64, I64, I64, P, I64]
         L.gpex_tiled_destroy.argtypes = [P]
         L.gpex_potrf_mp.argtypes = [P, P, C.POINTER(I64)]
         L.gpex_normals.argtypes = [P, U64, C.c_uint32, I64, I64, P, I64]
@@ -202,6 +203,12 @@ class Tiled:
         # column-major n x n == row-major transpose: out.T is the matrix
         self.ctx.check(lib().gpex_tiled_to_dense(self.ctx.h, self.h, _ptr(out), n))
         return out.T
+
+    def block(self, r0: int, c0: int, rows: int, cols: int):
+        """Unscaled sub-block [r0, r0+rows) x [c0, c0+cols) as a column-major rows x cols view."""
+        out = colmajor(rows, cols, self.ctx)
+        self.ctx.check(lib().gpex_tiled_block(self.ctx.h, self.h, r0, c0, rows, cols, _cm(out), rows))
+        return out
 
     def close(self):
         if self.h:

@@ -138,6 +138,13 @@ int gpex_tiled_stats(gpex_tiled_t t, double* h_stats);
  * dense n x n column-major d_out (leading dimension ld >= n); entries above the diagonal tiles
  * are set to 0.  Enqueued on ctx. */
 int gpex_tiled_to_dense(gpex_ctx_t ctx, gpex_tiled_t t, double* d_out, int64_t ld);
+/* Same conversion for the sub-block rows [r0, r0 + rows) x columns [c0, c0 + cols) of the n x n
+ * matrix (0 <= r0, c0; r0 + rows <= n; c0 + cols <= n) into d_out (rows x cols, leading
+ * dimension ld >= rows); parts above the diagonal tiles read as 0 (for a diagonal tile the
+ * stored upper triangle is copied: symmetric values before factorisation, zeros after).
+ * Used to check leading blocks and sampled rows of large factors.  Enqueued on ctx. */
+int gpex_tiled_block(gpex_ctx_t ctx, gpex_tiled_t t, int64_t r0, int64_t c0, int64_t rows,
+                     int64_t cols, double* d_out, int64_t ld);
 int gpex_tiled_destroy(gpex_tiled_t t);
 
 /* ---- mixed-precision tile Cholesky ------------------------------------------------------- */

@@ -116,6 +116,26 @@ def test_potrf_fp64(ctx, case):
     A.close()
 
 
+def test_tiled_block_matches_dense(ctx):
+    n, nb = 700, 128
+    x, y, params = setup_case(n, nb, 1.5, 0.1, 8)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=0)
+    D = A.to_dense().cpu().numpy()
+    for (r0, c0, nr, nc) in [(0, 0, 700, 700), (100, 37, 300, 250), (640, 0, 60, 700), (5, 600, 20, 100)]:
+        B = A.block(r0, c0, nr, nc).cpu().numpy()
+        ref = D[r0:r0 + nr, c0:c0 + nc].copy()
+        # above the diagonal tiles the block reads 0; inside diagonal tiles the stored symmetric part
+        for i in range(nr):
+            for j in range(nc):
+                if (c0 + j) // nb > (r0 + i) // nb:
+                    ref[i, j] = 0.0
+        np.testing.assert_array_equal(B, ref)
+    assert g.potrf_mp(ctx, A) == 0
+    L = A.to_dense().cpu().numpy()
+    np.testing.assert_array_equal(A.block(300, 0, 100, 400).cpu().numpy(), L[300:400, :400])
+    A.close()
+
+
 def test_potrf_reports_non_spd(ctx):
     # a negative diagonal entry at location 150 makes the pivot of column 151 negative
     n, nb = 300, 64
