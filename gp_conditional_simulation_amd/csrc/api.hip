@@ -113,6 +113,7 @@ extern "C" int gpex_tiled_destroy(gpex_tiled_t t) {
     (void)hipDeviceSynchronize();
     dev_free(t->base);
     dev_free(t->tinv);
+    dev_free(t->l16);
     delete t;
     return GPEX_OK;
 }

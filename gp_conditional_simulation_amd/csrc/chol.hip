@@ -210,6 +210,10 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     const size_t tile_el = (size_t)nb * nb;
     hipStream_t s = ctx->stream;
     if (!a->tinv) GPEX_TRY(dev_alloc(ctx, (void**)&a->tinv, sizeof(double) * tile_el * nt, "inverse diagonal tiles"));
+    // FP16 copy of the off-diagonal factor for the simulation product, written by the panel solves
+    if (a->opts.amp && nt > 1 && !a->l16)
+        GPEX_TRY(dev_alloc(ctx, (void**)&a->l16, sizeof(_Float16) * tile_el * (size_t)(nt * (nt - 1) / 2),
+                           "FP16 factor panels"));
     void* pws = nullptr;
     double* ws = nullptr;
     if (nt > 1) GPEX_TRY(dev_alloc(ctx, &pws, 8 * tile_el * (nt - 1), "panel workspace"));
@@ -253,6 +257,10 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             g.ta = (int8_t)p; g.tb = DT_F64; g.tc = (int8_t)p;
             g.transA = 0; g.transB = 1;
             g.alpha = 1.0; g.beta = 0.0;
+            if (a->l16) {   // tile (i, k) lands at columns [k nb, (k+1) nb) of row panel i
+                g.C2 = a->l16_panel(i) + (size_t)k * nb;
+                g.ldc2 = i * nb;
+            }
             panel[sig(DT_F64, g)].push_back(g);
         }
         for (int64_t j = k + 1; j < nt; ++j)

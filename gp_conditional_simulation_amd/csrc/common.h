@@ -39,6 +39,10 @@ struct gpex_tiled_s {
     double s = 1.0;
     std::vector<double> stats;       // 3 per lower tile: sum of squares, min, max (unscaled)
     double* tinv = nullptr;          // nt tiles nb x nb FP64: inverse of each diagonal factor tile
+    // FP16 copy of the off-diagonal factor for the simulation product (amp only): tile row i as one
+    // row-major panel of nb x (i nb) at l16 + nb*nb*i(i-1)/2 (k contiguous, leading dim i nb)
+    _Float16* l16 = nullptr;
+    _Float16* l16_panel(int64_t i) const { return l16 + (size_t)nb * nb * (size_t)(i * (i - 1) / 2); }
     bool factored = false;
     gpex_prec_opts opts{};
     gpex_diag diag{};
@@ -84,6 +88,10 @@ struct GemmTask {
     int M, N, K;
     int8_t ta, tb, tc, transA, transB, pad0, pad1, pad2;
     double alpha, beta;
+    // Optional second output (typed kernels only): the stored result converted to FP16 and
+    // written row-major, element (row, col) at C2[col + row * ldc2].
+    _Float16* C2;
+    int64_t ldc2;
 };
 
 // compute: DT_F64 (FP64 matrix cores), DT_F32 (FP32 matrix cores) or DT_F16 (FP16 matrix cores,

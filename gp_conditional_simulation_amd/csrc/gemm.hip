@@ -469,6 +469,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     }
 
     bool ovf = false;
+    _Float16* __restrict__ C2 = T.C2;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -479,26 +480,36 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
                 int col = n0 + wn * 64 + j * 16 + l % 16;
                 if (EDGE && (row >= T.M || col >= T.N)) continue;
                 int64_t ci = (int64_t)row + (int64_t)col * T.ldc;
+                double sv;   // the stored value, exactly, for the optional FP16 copy
                 if constexpr (sizeof(TC) == 8) {
                     double v = T.alpha * (double)acc[i][j][r];
                     if (T.beta != 0.0) v += T.beta * (double)Cp[ci];
                     Cp[ci] = v;
+                    sv = v;
                 } else if constexpr (sizeof(TC) == 4) {
                     float v = (float)T.alpha * (float)acc[i][j][r];
                     if (T.beta != 0.0) v += (float)T.beta * (float)Cp[ci];
                     Cp[ci] = v;
+                    sv = (double)v;
                 } else if constexpr (sizeof(CT) == 8) {
                     double v = T.alpha * acc[i][j][r];
                     if (T.beta != 0.0) v += T.beta * (double)Cp[ci];
                     _Float16 h = f64_to_f16(v);
                     if (__builtin_isinf((float)h) && !__builtin_isinf(v)) ovf = true;
                     Cp[ci] = h;
+                    sv = (double)h;
                 } else {
                     float v = (float)T.alpha * (float)acc[i][j][r];
                     if (T.beta != 0.0) v += (float)T.beta * (float)Cp[ci];
                     _Float16 h = (_Float16)v;
                     if (__builtin_isinf((float)h) && !__builtin_isinf(v)) ovf = true;
                     Cp[ci] = h;
+                    sv = (double)h;
+                }
+                if (C2) {
+                    _Float16 h2 = f64_to_f16(sv);
+                    C2[(int64_t)col + (int64_t)row * T.ldc2] = h2;
+                    if (__builtin_isinf((float)h2) && !__builtin_isinf(sv)) ovf = true;
                 }
             }
     if (ovf && flags) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
@@ -543,6 +554,7 @@ static int launch_ct(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
     int done = try_typed<CT, CT, CT, CT, 0, 1, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
     if (!done) done = try_typed<CT, CT, CT, CT, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
     if constexpr (sizeof(CT) == 2) {
+        if (!done) done = try_typed<CT, _Float16, _Float16, double, 1, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
         if (!done) done = try_typed<CT, double, _Float16, double, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
         if (!done) done = try_typed<CT, float, _Float16, double, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
         if (!done) done = try_typed<CT, _Float16, _Float16, double, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);

@@ -302,21 +302,60 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
                        1.0 / L->s, amp, B, part);
     if (hipGetLastError() != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "make_B launch"); }
     if (ctx->timing) (void)hipEventRecord(ev[1], s);
-    for (int64_t k = 0; k < nt; ++k) {
-        GemmTask g{};
-        g.A = L->tile(k, k); g.ta = DT_F64; g.lda = nb; g.transA = 0;
-        g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
-        g.ldb = rows; g.transB = 0;
-        g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
-        g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
-        g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
-        r = gemm_launch(ctx, s, amp ? DT_F32 : DT_F64, nullptr, 1, g, GEMM_TRMM);
-        for (int64_t gi = gbeg[(size_t)k]; r >= 0 && gi < gbeg[(size_t)k + 1]; ++gi) {
-            const Group& G = groups[(size_t)gi];
-            r = gemm_launch(ctx, s, amp ? DT_F16 : DT_F64, d_tasks + G.b0, (int)(G.b1 - G.b0), tasks[(size_t)G.b0],
-                            GEMM_TRMM);
+    if (amp && L->l16) {
+        // diagonal tiles: FP32 products of cast32(L_kk) and cast32(B_k), one launch
+        std::vector<GemmTask> dg;
+        for (int64_t k = 0; k < nt; ++k) {
+            GemmTask g{};
+            g.A = L->tile(k, k); g.ta = DT_F64; g.lda = nb; g.transA = 0;
+            g.B = static_cast<_Float16*>(B) + (size_t)k * nb; g.tb = DT_F16; g.ldb = rows; g.transB = 0;
+            g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
+            g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
+            g.alpha = 1.0; g.beta = 0.0;
+            dg.push_back(g);
         }
+        // off-diagonal part of tile row i: one FP16 product of the row panel (nb x i nb) with
+        // B[0 : i nb], longest rows first
+        std::vector<GemmTask> od;
+        for (int64_t i = nt - 1; i >= 1; --i) {
+            GemmTask g{};
+            g.A = L->l16_panel(i); g.ta = DT_F16; g.lda = i * nb; g.transA = 1;
+            g.B = B; g.tb = DT_F16; g.ldb = rows; g.transB = 0;
+            g.C = Mp + i * nb; g.tc = DT_F64; g.ldc = rows;
+            g.M = (int)nb; g.N = (int)cols; g.K = (int)(i * nb);
+            g.alpha = 1.0; g.beta = 1.0;
+            od.push_back(g);
+        }
+        GemmTask* d2 = nullptr;
+        r = dev_alloc(ctx, (void**)&d2, sizeof(GemmTask) * (dg.size() + od.size()), "trmm panel tasks");
+        if (r >= 0 && hipMemcpy(d2, dg.data(), sizeof(GemmTask) * dg.size(), hipMemcpyHostToDevice) != hipSuccess)
+            r = set_err(ctx, GPEX_ERR_HIP, "trmm task upload");
+        if (r >= 0 && !od.empty() &&
+            hipMemcpy(d2 + dg.size(), od.data(), sizeof(GemmTask) * od.size(), hipMemcpyHostToDevice) != hipSuccess)
+            r = set_err(ctx, GPEX_ERR_HIP, "trmm task upload");
+        if (r >= 0) r = gemm_launch(ctx, s, DT_F32, d2, (int)dg.size(), dg[0], GEMM_TRMM);
+        if (r >= 0 && !od.empty()) r = gemm_launch(ctx, s, DT_F16, d2 + dg.size(), (int)od.size(), od[0], GEMM_TRMM);
+        // d2 is released after the stream synchronisation below
+        dev_free(d_tasks);
+        d_tasks = d2;
         if (r < 0) { cleanup(); return r; }
+    } else {
+        for (int64_t k = 0; k < nt; ++k) {
+            GemmTask g{};
+            g.A = L->tile(k, k); g.ta = DT_F64; g.lda = nb; g.transA = 0;
+            g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
+            g.ldb = rows; g.transB = 0;
+            g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
+            g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
+            g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
+            r = gemm_launch(ctx, s, amp ? DT_F32 : DT_F64, nullptr, 1, g, GEMM_TRMM);
+            for (int64_t gi = gbeg[(size_t)k]; r >= 0 && gi < gbeg[(size_t)k + 1]; ++gi) {
+                const Group& G = groups[(size_t)gi];
+                r = gemm_launch(ctx, s, amp ? DT_F16 : DT_F64, d_tasks + G.b0, (int)(G.b1 - G.b0), tasks[(size_t)G.b0],
+                                GEMM_TRMM);
+            }
+            if (r < 0) { cleanup(); return r; }
+        }
     }
     if (ctx->timing) (void)hipEventRecord(ev[2], s);
     r = copy2d(ctx, s, Mp, DT_F64, rows, d_M, DT_F64, ldm, n, nsim, 1.0);
