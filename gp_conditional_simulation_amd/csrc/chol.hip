@@ -227,7 +227,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     // tasks of one step with one compute precision and one operand-type signature (a launch runs
     // one typed kernel).  Panel solves: FP64 compute for every tile; updates: the output tile's
     // precision.
-    struct Group { int64_t b0, b1; int compute, role, k; };
+    struct Group { int64_t b0, b1; int compute, role, k, next; };
     std::vector<GemmTask> tasks;
     std::vector<CopyTask> copies;
     std::vector<Group> groups;
@@ -245,7 +245,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         }
         copy_beg[(size_t)k + 1] = (int64_t)copies.size();
         group_beg[(size_t)k] = (int64_t)groups.size();
-        std::map<int, std::vector<GemmTask>> panel, update;
+        std::map<int, std::vector<GemmTask>> panel, update, update_next;
         for (int64_t i = k + 1; i < nt; ++i) {
             int p = a->prec(i, k);
             GemmTask g{};
@@ -275,19 +275,20 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
                 g.ta = (int8_t)a->prec(i, k); g.tb = (int8_t)a->prec(j, k); g.tc = (int8_t)p;
                 g.transA = 0; g.transB = 1;
                 g.alpha = -1.0; g.beta = 1.0;
-                update[sig(p, g)].push_back(g);
+                (j == k + 1 ? update_next : update)[sig(p, g)].push_back(g);
                 upd_flops[(size_t)p] += (i == j ? 1.0 : 2.0) * nb * (double)nb * nb;
             }
         for (auto& kv : panel) {
-            groups.push_back(Group{(int64_t)tasks.size(), 0, DT_F64, GEMM_GENERIC, (int)k});
+            groups.push_back(Group{(int64_t)tasks.size(), 0, DT_F64, GEMM_GENERIC, (int)k, 0});
             tasks.insert(tasks.end(), kv.second.begin(), kv.second.end());
             groups.back().b1 = (int64_t)tasks.size();
         }
-        for (auto& kv : update) {
-            groups.push_back(Group{(int64_t)tasks.size(), 0, kv.first / 1000, GEMM_UPDATE, (int)k});
-            tasks.insert(tasks.end(), kv.second.begin(), kv.second.end());
-            groups.back().b1 = (int64_t)tasks.size();
-        }
+        for (int nx = 1; nx >= 0; --nx)
+            for (auto& kv : (nx ? update_next : update)) {
+                groups.push_back(Group{(int64_t)tasks.size(), 0, kv.first / 1000, GEMM_UPDATE, (int)k, nx});
+                tasks.insert(tasks.end(), kv.second.begin(), kv.second.end());
+                groups.back().b1 = (int64_t)tasks.size();
+            }
     }
     group_beg[(size_t)nt] = (int64_t)groups.size();
     GemmTask* d_tasks = nullptr;
@@ -323,38 +324,98 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         e_all0 = tm.next();
         (void)hipEventRecord(e_all0, s);
     }
+    // Look-ahead of depth one on two streams (both at the default priority):
+    //   stream A (the context stream): [wait rest(k-1)] next-column update of step k, then the panel
+    //            work of step k+1 (diagonal factor + inverse, panel copy, panel solves);
+    //   stream B: [wait panel(k)] the rest of step k's trailing update.
+    // The panel work of step k+1 thus overlaps the bulk update of step k.  Tiles touched
+    // concurrently are disjoint: rest(k) writes columns >= k+2, the panel of k+1 column k+1.
+    hipStream_t sb = nullptr;
+    hipEvent_t evfork = nullptr;
+    std::vector<hipEvent_t> evp((size_t)nt, nullptr), evr((size_t)nt, nullptr);
+    auto release_sync = [&]() {
+        if (evfork) (void)hipEventDestroy(evfork);
+        for (auto e : evp) if (e) (void)hipEventDestroy(e);
+        for (auto e : evr) if (e) (void)hipEventDestroy(e);
+        if (sb) (void)hipStreamDestroy(sb);
+    };
+    if (hipStreamCreateWithFlags(&sb, hipStreamNonBlocking) != hipSuccess) {
+        cleanup_all();
+        return set_err(ctx, GPEX_ERR_HIP, "potrf: second stream");
+    }
+    if (hipEventCreateWithFlags(&evfork, hipEventDisableTiming) != hipSuccess) {
+        release_sync();
+        cleanup_all();
+        return set_err(ctx, GPEX_ERR_HIP, "potrf: events");
+    }
     for (int64_t k = 0; k < nt; ++k) {
-        POTRF_TRY(potrf_inv(ctx, s, static_cast<double*>(a->tile(k, k)), nb, a->tinv_tile(k), nb, nb, ws, k * nb));
-        if (k == nt - 1) break;
+        if (hipEventCreateWithFlags(&evp[(size_t)k], hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&evr[(size_t)k], hipEventDisableTiming) != hipSuccess) {
+            release_sync();
+            cleanup_all();
+            return set_err(ctx, GPEX_ERR_HIP, "potrf: events");
+        }
+    }
+#define POTRF_TRY2(expr)                                   \
+    do {                                                   \
+        int r2_ = (expr);                                  \
+        if (r2_ < 0) { (void)hipStreamSynchronize(sb); (void)hipStreamSynchronize(s); release_sync(); cleanup_all(); return r2_; } \
+    } while (0)
+    auto launch_groups = [&](int64_t k, int want_role, int want_next, hipStream_t st) -> int {
+        for (int64_t gi = group_beg[(size_t)k]; gi < group_beg[(size_t)k + 1]; ++gi) {
+            const Group& G = groups[(size_t)gi];
+            if (G.role != want_role || (want_role == GEMM_UPDATE && G.next != want_next)) continue;
+            const bool upd = G.role == GEMM_UPDATE;
+            Rec rc{nullptr, nullptr, G.compute};
+            if (ctx->timing && upd) {
+                rc.b = tm.next();
+                (void)hipEventRecord(rc.b, st);
+            }
+            int r = gemm_launch(ctx, st, G.compute, d_tasks + G.b0, (int)(G.b1 - G.b0), tasks[(size_t)G.b0], G.role);
+            if (r < 0) return r;
+            if (ctx->timing && upd) {
+                rc.e = tm.next();
+                (void)hipEventRecord(rc.e, st);
+                recs.push_back(rc);
+            }
+        }
+        return GPEX_OK;
+    };
+    auto panel_work = [&](int64_t k) -> int {
+        GPEX_TRY(potrf_inv(ctx, s, static_cast<double*>(a->tile(k, k)), nb, a->tinv_tile(k), nb, nb, ws, k * nb));
         int64_t nc = copy_beg[(size_t)k + 1] - copy_beg[(size_t)k];
         if (nc > 0) {
             const int64_t chunk = 1 << 16;
             int64_t mx = (int64_t)(8 * tile_el);
             dim3 grid((unsigned)((mx + chunk - 1) / chunk), (unsigned)nc);
             hipLaunchKernelGGL(k_copy_tasks, grid, dim3(256), 0, s, d_copies + copy_beg[(size_t)k], chunk);
-            POTRF_TRY(hipGetLastError() == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "panel copy launch"));
+            GPEX_HIP(ctx, hipGetLastError());
         }
-        for (int64_t gi = group_beg[(size_t)k]; gi < group_beg[(size_t)k + 1]; ++gi) {
-            const Group& G = groups[(size_t)gi];
-            const bool upd = G.role == GEMM_UPDATE;
-            Rec rc{nullptr, nullptr, G.compute};
-            if (ctx->timing && upd) {
-                rc.b = tm.next();
-                (void)hipEventRecord(rc.b, s);
-            }
-            POTRF_TRY(gemm_launch(ctx, s, G.compute, d_tasks + G.b0, (int)(G.b1 - G.b0), tasks[(size_t)G.b0], G.role));
-            if (ctx->timing && upd) {
-                rc.e = tm.next();
-                (void)hipEventRecord(rc.e, s);
-                recs.push_back(rc);
-            }
-        }
+        return launch_groups(k, GEMM_GENERIC, 0, s);
+    };
+    // fork: stream B starts after everything queued so far on the context stream
+    POTRF_TRY2(hipEventRecord(evfork, s) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "fork"));
+    POTRF_TRY2(hipStreamWaitEvent(sb, evfork, 0) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "fork"));
+    POTRF_TRY2(panel_work(0));
+    POTRF_TRY2(hipEventRecord(evp[0], s) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "event"));
+    for (int64_t k = 0; k + 1 < nt; ++k) {
+        if (k > 0) POTRF_TRY2(hipStreamWaitEvent(s, evr[(size_t)k - 1], 0) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "wait"));
+        POTRF_TRY2(launch_groups(k, GEMM_UPDATE, 1, s));
+        POTRF_TRY2(panel_work(k + 1));
+        POTRF_TRY2(hipEventRecord(evp[(size_t)k + 1], s) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "event"));
+        POTRF_TRY2(hipStreamWaitEvent(sb, evp[(size_t)k], 0) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "wait"));
+        POTRF_TRY2(launch_groups(k, GEMM_UPDATE, 0, sb));
+        POTRF_TRY2(hipEventRecord(evr[(size_t)k], sb) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "event"));
     }
+    // join: the context stream waits for the last bulk update
+    if (nt > 1) POTRF_TRY2(hipStreamWaitEvent(s, evr[(size_t)nt - 2], 0) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "join"));
     if (ctx->timing) {
         e_all1 = tm.next();
         (void)hipEventRecord(e_all1, s);
     }
     hipError_t se = hipStreamSynchronize(s);
+    if (se == hipSuccess) se = hipStreamSynchronize(sb);
+    release_sync();
     if (se != hipSuccess) {
         cleanup_all();
         return set_err(ctx, GPEX_ERR_HIP, std::string("potrf sync: ") + hipGetErrorString(se));
