@@ -38,14 +38,16 @@ class CovParams(C.Structure):
 
 
 class PrecOpts(C.Structure):
-    _fields_ = [("amp", C.c_int), ("tol", C.c_double), ("allow_fp16", C.c_int), ("unscaled_rule", C.c_int)]
+    _fields_ = [("amp", C.c_int), ("tol", C.c_double), ("allow_fp16", C.c_int), ("unscaled_rule", C.c_int),
+                ("auto_tol", C.c_int)]
 
 
 class Diag(C.Structure):
     _fields_ = [("s", C.c_double), ("frob", C.c_double), ("l_bound", C.c_double), ("u_bound", C.c_double),
                 ("l_bound_sub", C.c_double), ("r_hp", C.c_double), ("rho1", C.c_double), ("rho2", C.c_double),
                 ("norm_B", C.c_double), ("eq10_pass", C.c_int), ("eq11_pass", C.c_int),
-                ("lower_exceeds_upper", C.c_int), ("fp16_overflow", C.c_int), ("tiles", C.c_int64 * 3)]
+                ("lower_exceeds_upper", C.c_int), ("fp16_overflow", C.c_int), ("tiles", C.c_int64 * 3),
+                ("tol", C.c_double), ("tol_reductions", C.c_int64)]
 
     def to_dict(self) -> dict:
         d = {k: getattr(self, k) for k, _ in self._fields_ if k != "tiles"}
@@ -223,14 +225,14 @@ class Tiled:
 
 
 def cov_gen(ctx: Context, loc, n: int, params: dict, nb: int, amp: int = 0, tol: float = 0.0,
-            allow_fp16: bool = True, nt_rule: bool = True, diag_add=None) -> Tiled:
+            allow_fp16: bool = True, nt_rule: bool = True, diag_add=None, auto_tol: bool = False) -> Tiled:
     """gpex_cov_gen.  loc: float64 device tensor of 2n values (x then y)."""
     import torch
     _dev_check(loc, ctx, torch.float64)
     _dev_check(diag_add, ctx, torch.float64)
     cp = CovParams(int(params.get("kind", 0)), float(params["sigma2"]), float(params["range"]),
                    float(params.get("nu", 0.5)), float(params.get("nugget", 0.0)))
-    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(not nt_rule))
+    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(not nt_rule), int(auto_tol))
     h = C.c_void_p()
     d = Diag()
     rc = lib().gpex_cov_gen(ctx.h, _ptr(loc), n, _ptr(diag_add), C.byref(cp), nb, C.byref(po), C.byref(h),
@@ -257,13 +259,14 @@ def normals(ctx: Context, seed: int, stream: int, n: int, nsim: int, out=None):
     return out
 
 
-def plan(stats, nt: int, amp: int = 1, tol: float = 0.0, allow_fp16: bool = True, nt_rule: bool = True):
+def plan(stats, nt: int, amp: int = 1, tol: float = 0.0, allow_fp16: bool = True, nt_rule: bool = True,
+         auto_tol: bool = False):
     """gpex_plan (host only): precision map and diagnostics from tile statistics."""
     st = np.ascontiguousarray(stats, dtype=np.float64).reshape(-1)
     if st.size != 3 * nt * (nt + 1) // 2:
         raise ValueError("stats must hold 3 values per lower tile")
     pmap = np.zeros((nt, nt), dtype=np.uint8)
-    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(not nt_rule))
+    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(not nt_rule), int(auto_tol))
     d = Diag()
     rc = lib().gpex_plan(st.ctypes.data, nt, C.byref(po), pmap.ctypes.data, C.byref(d))
     if rc != 0:

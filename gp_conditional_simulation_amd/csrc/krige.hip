@@ -139,7 +139,7 @@ extern "C" int gpex_krige(gpex_ctx_t ctx, const double* d_loc_o, int64_t n_o, co
     *info = 0;
     gpex_cov_params cp = *params;
     cp.nugget = tau2;
-    gpex_prec_opts po{0, 0.0, 0, 0};
+    gpex_prec_opts po{0, 0.0, 0, 0, 0};
     gpex_tiled_t Sy = nullptr;
     int r = gpex_cov_gen(ctx, d_loc_o, n_o, nullptr, &cp, nb, &po, &Sy, nullptr);
     if (r < 0) return r;

@@ -19,8 +19,8 @@
 
 namespace gpex {
 
-void plan_precision(const std::vector<double>& st, int64_t nt, const gpex_prec_opts& o,
-                    std::vector<uint8_t>& map, gpex_diag& d) {
+static void plan_once(const std::vector<double>& st, int64_t nt, const gpex_prec_opts& o,
+                      std::vector<uint8_t>& map, gpex_diag& d) {
     const double eps16 = std::ldexp(1.0, -10), eps32 = std::ldexp(1.0, -23);
     const double xmax32 = (2.0 - std::ldexp(1.0, -23)) * std::ldexp(1.0, 127), xmax16 = 65504.0;
     const double xnorm32 = std::ldexp(1.0, -126), xnorm16 = std::ldexp(1.0, -14);
@@ -108,6 +108,28 @@ void plan_precision(const std::vector<double>& st, int64_t nt, const gpex_prec_o
     d.lower_exceeds_upper = l > d.u_bound;
     double sc = std::floor(d.u_bound) - 1.0;
     d.s = sc > 1.0 ? sc : 1.0;
+}
+
+// Sec. V-D automatic mode: fixedacc starts at 1e-4 and is reduced by a factor of 0.9 whenever
+// either check fails; iteration stops when both pass or no FP16 tile remains.  A tile whose norm
+// is exactly zero would stay FP16 at any tolerance, so the loop is capped at 2000 reductions.
+void plan_precision(const std::vector<double>& st, int64_t nt, const gpex_prec_opts& o,
+                    std::vector<uint8_t>& map, gpex_diag& d) {
+    gpex_prec_opts q = o;
+    int64_t red = 0;
+    if (o.amp && o.auto_tol) {
+        q.tol = 1e-4;
+        for (;;) {
+            plan_once(st, nt, q, map, d);
+            if ((d.eq10_pass && d.eq11_pass) || d.tiles[DT_F16] == 0 || red >= 2000) break;
+            q.tol *= 0.9;
+            ++red;
+        }
+    } else {
+        plan_once(st, nt, q, map, d);
+    }
+    d.tol = q.tol;
+    d.tol_reductions = red;
 }
 
 }  // namespace gpex

@@ -66,12 +66,16 @@ typedef struct {
 /* Precision options.  amp = 0: every tile FP64 and s = 1 (Algorithm 1, AMP = 0 branch).
  * amp = 1: with r = ||V_ij||_F / ||V||_F and NT tile rows, off-diagonal tile (i, j) goes to FP16
  * when allow_fp16 and r * NT * 2^-10 <= tol, else to FP32 when r * NT * 2^-23 <= tol, else stays
- * FP64; unscaled_rule != 0 drops the NT factor (r * eps <= tol).  tol is the pages' fixedacc. */
+ * FP64; unscaled_rule != 0 drops the NT factor (r * eps <= tol).  tol is the pages' fixedacc.
+ * auto_tol != 0 (automatic mode, Sec. V-D): tol starts at 1e-4 (the given tol is ignored) and is
+ * multiplied by 0.9 while Eq. 10 or Eq. 11 fails and FP16 tiles remain (at most 2000 rounds);
+ * the final tol and the number of reductions are reported in gpex_diag. */
 typedef struct {
     int amp;
     double tol;
     int allow_fp16;
     int unscaled_rule;
+    int auto_tol;
 } gpex_prec_opts;
 
 /* Diagnostics of the plan (Sec. V-D, V-E) and of the simulation input (Algorithm 1). */
@@ -86,6 +90,8 @@ typedef struct {
     double norm_B;        /* ||Z / s||_F of the simulation input (gpex_trmm_sim) */
     int eq10_pass, eq11_pass, lower_exceeds_upper, fp16_overflow;
     int64_t tiles[3];     /* lower tiles per precision: FP64, FP32, FP16 */
+    double tol;           /* tolerance the map was built with (the final one in automatic mode) */
+    int64_t tol_reductions; /* automatic mode: number of 0.9 reductions applied */
 } gpex_diag;
 
 typedef struct {
@@ -123,8 +129,9 @@ int gpex_cov_gen(gpex_ctx_t ctx, const double* d_loc, int64_t n, const double* d
 /* Host-only planning from tile statistics (no device work): h_stats holds 3*nt*(nt+1)/2 doubles
  * (sum of squares, min, max per lower tile, row-packed), h_map receives nt*nt bytes (row-major,
  * 255 above the diagonal), diag the Eq. 10/11 values and the Eq. 12 scale.  This is the plan
- * gpex_cov_gen applies; it lets a caller re-plan cached statistics under another tolerance.
- * Returns GPEX_OK or GPEX_ERR_ARG. */
+ * gpex_cov_gen applies; it lets a caller re-plan cached statistics under another tolerance (or
+ * run the automatic refinement) without regenerating the matrix, and reuse a final tolerance
+ * from an earlier automatic run.  Returns GPEX_OK or GPEX_ERR_ARG. */
 int gpex_plan(const double* h_stats, int64_t nt, const gpex_prec_opts* opts, uint8_t* h_map,
               gpex_diag* diag);
 

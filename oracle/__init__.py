@@ -22,7 +22,7 @@ import os
 import numpy as np
 
 from . import build as _build
-from .planner import plan, PlanResult  # noqa: F401
+from .planner import plan, plan_auto, PlanResult  # noqa: F401
 from .regions import empirical_quantile, quantile_index, calibrate  # noqa: F401
 
 _lib = None

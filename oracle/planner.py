@@ -35,6 +35,11 @@ EQ10_LIMIT = 65504.0 / 2.0 ** -24          # printed as "approximately 1.10 x 10
 EQ11_LIMIT = 1e-4 / 2.0 ** -10
 
 
+AUTO_START = 1e-4        # Sec. V-D: automatic mode starts at fixedacc = 10^-4 ...
+AUTO_FACTOR = 0.9        # ... and multiplies it by 0.9 whenever a check fails
+AUTO_MAX = 2000          # guard: a tile with zero norm would stay FP16 at every tolerance
+
+
 @dataclasses.dataclass
 class PlanResult:
     pmap: np.ndarray            # uint8 [NT, NT]
@@ -50,6 +55,22 @@ class PlanResult:
     eq10_pass: bool
     eq11_pass: bool
     tiles: tuple                # (n FP64, n FP32, n FP16) over the lower triangle
+    tol: float = 0.0            # tolerance of this map (the final one in automatic mode)
+    reductions: int = 0         # automatic mode: number of 0.9 reductions
+
+
+def plan_auto(stats: np.ndarray, nt: int, allow_fp16: bool = True, nt_rule: bool = True) -> PlanResult:
+    """Automatic fixedacc refinement (Sec. V-D): start at 1e-4, multiply by 0.9 while Eq. 10 or
+    Eq. 11 fails, stop when both pass or no FP16 tile remains."""
+    tol = AUTO_START
+    k = 0
+    while True:
+        r = plan(stats, nt, tol, amp=1, allow_fp16=allow_fp16, nt_rule=nt_rule)
+        if (r.eq10_pass and r.eq11_pass) or r.tiles[2] == 0 or k >= AUTO_MAX:
+            r.tol, r.reductions = tol, k
+            return r
+        tol *= AUTO_FACTOR
+        k += 1
 
 
 def plan(stats: np.ndarray, nt: int, tol: float, amp: int = 1, allow_fp16: bool = True,
@@ -77,7 +98,7 @@ def plan(stats: np.ndarray, nt: int, tol: float, amp: int = 1, allow_fp16: bool 
     lower = [(i, j) for i in range(nt) for j in range(i + 1)]
     counts = tuple(sum(1 for (i, j) in lower if pmap[i, j] == p) for p in (FP64, FP32, FP16))
     if not amp:
-        return PlanResult(pmap, 1.0, frob, 0.0, 1.0, False, 0.0, float("nan"), 0.0, 0.0, True, True, counts)
+        return PlanResult(pmap, 1.0, frob, 0.0, 1.0, False, 0.0, float("nan"), 0.0, 0.0, True, True, counts, tol)
 
     def st(i, j):
         return stats[i * (i + 1) // 2 + j]
@@ -116,4 +137,4 @@ def plan(stats: np.ndarray, nt: int, tol: float, amp: int = 1, allow_fp16: bool 
     u_s = min(65504.0, u_min)
     s_cand = math.floor(u_s) - 1.0
     s = s_cand if s_cand > 1.0 else 1.0
-    return PlanResult(pmap, s, frob, l_b, u_s, l_b > u_s, l_sub, r_hp, rho1, rho2, eq10, eq11, counts)
+    return PlanResult(pmap, s, frob, l_b, u_s, l_b > u_s, l_sub, r_hp, rho1, rho2, eq10, eq11, counts, tol)

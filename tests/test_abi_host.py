@@ -66,6 +66,26 @@ def test_host_planner_equals_oracle_planner(seed, tol):
             assert bool(d["lower_exceeds_upper"]) == r.lower_exceeds_upper
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_host_planner_automatic_mode_equals_oracle(seed):
+    nt = 4 + seed * 2
+    st = _random_stats(nt, 100 + seed)
+    pm, d = g.plan(st, nt, amp=1, auto_tol=True)
+    r = oracle.plan_auto(st, nt)
+    low = np.tril_indices(nt)
+    assert np.array_equal(pm[low], r.pmap[low])
+    assert d["tol"] == r.tol and d["tol_reductions"] == r.reductions and d["s"] == r.s
+
+
+def test_host_planner_automatic_worked_example():
+    gold = json.load(open(os.path.join(ROOT, "tests", "golden", "planner_auto_example.json")))
+    pm, d = g.plan(np.array(gold["stats"]), gold["nt"], amp=1, auto_tol=True)
+    assert d["tol_reductions"] == gold["reductions"]
+    assert d["tol"] == pytest.approx(gold["tol"], rel=1e-12)
+    for i, row in enumerate(gold["pmap_lower"]):
+        assert pm[i, :i + 1].tolist() == row
+
+
 def test_host_planner_worked_example_and_amp0():
     gold = json.load(open(os.path.join(ROOT, "tests", "golden", "planner_worked_example.json")))
     st = np.array(gold["stats"])

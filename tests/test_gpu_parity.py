@@ -186,6 +186,19 @@ def test_potrf_and_trmm_mixed_precision(ctx, case):
     A.close()
 
 
+def test_automatic_tolerance_from_device_stats(ctx):
+    n, nb = 3000, 160
+    x, y, params = setup_case(n, nb, 1.5, 0.03, 12)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, auto_tol=True)
+    r = oracle.plan_auto(A.stats(), A.info()["nt"])
+    low = np.tril_indices(A.info()["nt"])
+    assert np.array_equal(A.info()["map"][low], r.pmap[low])
+    assert A.diag["tol"] == r.tol and A.diag["tol_reductions"] == r.reductions
+    assert A.status == g.OK and A.diag["eq10_pass"] and A.diag["eq11_pass"]
+    assert g.potrf_mp(ctx, A) == 0
+    A.close()
+
+
 def test_loose_tolerance_reports_failed_checks(ctx):
     # tol 1e-4 sends even the tiles beside the diagonal to FP16: Eq. 11 fails and, with a user
     # tolerance, the failure is reported (Sec. V-D) while the factorisation still runs

@@ -406,6 +406,32 @@ def test_planner_rule_variants_worked_example():
         assert rs.pmap[i, :i + 1].tolist() == rc["scaled_pmap_lower"][i]
 
 
+def test_planner_automatic_refinement_worked_example():
+    g = _gold("planner_auto_example.json")
+    r = oracle.plan_auto(np.array(g["stats"]), g["nt"])
+    assert r.reductions == g["reductions"]
+    assert r.tol == pytest.approx(g["tol"], rel=1e-12)
+    for i, row in enumerate(g["pmap_lower"]):
+        assert r.pmap[i, :i + 1].tolist() == row
+    assert r.eq10_pass and r.eq11_pass
+    # one reduction fewer still fails Eq. 11
+    r16 = oracle.plan(np.array(g["stats"]), g["nt"], 1e-4 * 0.9 ** 16)
+    assert not r16.eq11_pass and r16.pmap[1, 0] == 2
+
+
+def test_planner_automatic_refinement_stops_without_fp16():
+    # a tile with a negative minimum fails Eq. 10 while it is FP16; the loop must run until the
+    # tile leaves FP16: r = 1e-3/sqrt(200 + 2e-6) = 7.071e-5, r*2*2^-10 = 1.381e-7, so
+    # 1e-4 * 0.9^k < 1.381e-7 first holds at k = 63
+    st = np.array([[100.0, 0.5, 1.0], [1e-6, -1e-3, 1e-3], [100.0, 0.5, 1.0]])
+    assert oracle.plan(st, 2, 1e-4).tiles[2] == 1
+    r = oracle.plan_auto(st, 2)
+    assert r.tiles[2] == 0 and r.reductions == 63
+    assert oracle.plan(st, 2, r.tol / 0.9).tiles[2] == 1
+    # no FP16 tile at the start: no reduction
+    assert oracle.plan_auto(np.array([[100.0, 0.5, 1.0], [50.0, 0.2, 0.9], [100.0, 0.5, 1.0]]), 2).reductions == 0
+
+
 def test_planner_edge_cases():
     st = np.array([[100.0, 0.5, 1.0], [50.0, 0.2, 0.9], [100.0, 0.5, 1.0]])
     r0 = oracle.plan(st, 2, 1e-8, amp=0)
