@@ -100,6 +100,7 @@ struct GemmTask {
 // `one` passed by value.  A task whose types differ from `one`'s sets flags[FLAG_BADTASK] and
 // is skipped.
 enum : int { GEMM_GENERIC = 0, GEMM_UPDATE = 1, GEMM_TRMM = 2 };
+extern int g_f16_grid;   // wave grid of FP16 TRMM launches (-1 auto, 0: 2 x 2, 1: 4 x 2, 2: 2 x 4)
 int gemm_launch(gpex_ctx_t ctx, hipStream_t s, int compute, const GemmTask* d_tasks, int ntasks,
                 const GemmTask& one, int role = GEMM_GENERIC);
 

@@ -31,6 +31,10 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 128, BN = 128, NTHR = 256;
 
+// Wave grid of FP16 TRMM launches: -1 = chosen per launch (2 x 4 waves when that still gives at
+// least 2048 workgroups, else 2 x 2), 0 = 2 x 2 waves (128 x 128), 1 = 4 x 2, 2 = 2 x 4.
+int g_f16_grid = -1;
+
 template <typename CT> struct Cfg;
 template <> struct Cfg<double> { static constexpr int BK = 16, PAD = 2; };
 template <> struct Cfg<float> { static constexpr int BK = 16, PAD = 4; };
@@ -299,25 +303,26 @@ template <> __device__ __forceinline__ _Float16 to_ct<_Float16, double>(double v
 template <> __device__ __forceinline__ _Float16 to_ct<_Float16, float>(float v) { return (_Float16)v; }
 template <> __device__ __forceinline__ _Float16 to_ct<_Float16, _Float16>(_Float16 v) { return v; }
 
-template <typename T> struct V4;
-template <> struct V4<double> { typedef double __attribute__((ext_vector_type(4))) type; };
-template <> struct V4<float> { typedef float __attribute__((ext_vector_type(4))) type; };
-template <> struct V4<_Float16> { typedef _Float16 __attribute__((ext_vector_type(4))) type; };
+template <typename T, int N> struct VN { typedef T __attribute__((ext_vector_type(N))) type; };
 
 // One operand slab (128 rows x BK) of the typed kernel.  CR: the row index is contiguous in
 // global memory.  LDS layout: FP64/FP32 operands with CR are kept as [k][row] (row stride LDR,
 // padded so that the four lane groups of a fragment read hit different banks; stores are plain
 // vector writes); all other operands as [row][k] (k contiguous, the FP16 fragments need 8
 // consecutive k per lane).
-template <typename CT, typename T, bool CR, bool EDGE>
+template <typename CT, typename T, bool CR, bool EDGE, int ROWS = 128, int THREADS = NTHR>
 struct TSlab {
     static constexpr int BK = TCfg<CT>::BK;
     static constexpr bool KROW = CR && sizeof(CT) >= 4;        // [k][row] layout
     static constexpr int LDK = BK + TCfg<CT>::PAD;               // [row][k] row stride
-    static constexpr int LDR = 128 + (sizeof(CT) == 8 ? 4 : 8);  // [k][row] k stride
-    static constexpr int ELEMS = KROW ? BK * LDR : 128 * LDK;
-    static constexpr int VPT = (128 * BK / NTHR) / 4;
-    CT v[VPT][4];
+    static constexpr int LDR = ROWS + (sizeof(CT) == 8 ? 4 : 8); // [k][row] k stride
+    static constexpr int ELEMS = KROW ? BK * LDR : ROWS * LDK;
+    // elements per vector: 16-byte loads for k-contiguous FP16 operands, else 4 elements
+    static constexpr int VE = (!CR && sizeof(T) == 2 && sizeof(CT) == 2) ? 8 : 4;
+    static constexpr int VPT = (ROWS * BK / THREADS) / VE;
+    static constexpr int TPK = ROWS / VE;                         // threads per k-row (CR)
+    static_assert(VPT >= 1 && (ROWS * BK) % (THREADS * VE) == 0, "slab must split evenly over the threads");
+    CT v[VPT][VE];
 
     __device__ __forceinline__ static int idx(int row, int k) { return KROW ? k * LDR + row : row * LDK + k; }
 
@@ -326,22 +331,23 @@ struct TSlab {
         for (int q = 0; q < VPT; ++q) {
             int r, k;
             if (CR) {
-                r = (t % 32) * 4;
-                k = t / 32 + 8 * q;
+                r = (t % TPK) * VE;
+                k = t / TPK + (THREADS / TPK) * q;
             } else {
-                constexpr int TPR = BK / 4;
-                r = t / TPR + (NTHR / TPR) * q;
-                k = (t % TPR) * 4;
+                constexpr int TPR = BK / VE;
+                r = t / TPR + (THREADS / TPR) * q;
+                k = (t % TPR) * VE;
             }
             int gr = r0 + r, gk = k0 + k;
             if (!EDGE) {
                 int64_t id = CR ? (int64_t)gr + (int64_t)gk * ld : (int64_t)gk + (int64_t)gr * ld;
-                typename V4<T>::type x = *reinterpret_cast<const __attribute__((address_space(1))) typename V4<T>::type*>(base + id);
+                typedef typename VN<T, VE>::type VT;
+                VT x = *reinterpret_cast<const __attribute__((address_space(1))) VT*>(base + id);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[q][e] = to_ct<CT, T>(x[e]);
+                for (int e = 0; e < VE; ++e) v[q][e] = to_ct<CT, T>(x[e]);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < VE; ++e) {
                     int rr = CR ? gr + e : gr;
                     int kk = CR ? gk : gk + e;
                     v[q][e] = (rr < R && kk < K)
@@ -356,28 +362,31 @@ struct TSlab {
 #pragma unroll
         for (int q = 0; q < VPT; ++q) {
             if (CR) {
-                int r = (t % 32) * 4, k = t / 32 + 8 * q;
+                int r = (t % TPK) * VE, k = t / TPK + (THREADS / TPK) * q;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm[idx(r + e, k)] = v[q][e];
+                for (int e = 0; e < VE; ++e) sm[idx(r + e, k)] = v[q][e];
             } else {
-                constexpr int TPR = BK / 4;
-                int r = t / TPR + (NTHR / TPR) * q, k = (t % TPR) * 4;
+                constexpr int TPR = BK / VE;
+                int r = t / TPR + (THREADS / TPR) * q, k = (t % TPR) * VE;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm[idx(r, k + e)] = v[q][e];
+                for (int e = 0; e < VE; ++e) sm[idx(r, k + e)] = v[q][e];
             }
         }
     }
 };
 
-template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, bool EDGE, int ROLE>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// WMW x WNW waves of 64 x 64 each: a block of (64 WMW) x (64 WNW) outputs per workgroup.
+template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, bool EDGE, int ROLE,
+          int WMW = 2, int WNW = 2>
+__global__ __launch_bounds__(64 * WMW * WNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int bmc, int bnc, int xcd_map,
               unsigned long long* flags) {
     constexpr int BK = TCfg<CT>::BK;
+    constexpr int TBM = 64 * WMW, TBN = 64 * WNW, THR = 64 * WMW * WNW;
     constexpr bool a_contig_r = TRA == 0;
     constexpr bool b_contig_r = TRB != 0;
-    typedef TSlab<CT, TA, a_contig_r, EDGE> SA;
-    typedef TSlab<CT, TB, b_contig_r, EDGE> SB;
+    typedef TSlab<CT, TA, a_contig_r, EDGE, TBM, THR> SA;
+    typedef TSlab<CT, TB, b_contig_r, EDGE, TBN, THR> SB;
     __shared__ __attribute__((aligned(16))) CT As[2][SA::ELEMS];
     __shared__ __attribute__((aligned(16))) CT Bs[2][SB::ELEMS];
 
@@ -403,9 +412,9 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     gptr<TA> Ap = (gptr<TA>)T.A;
     gptr<TB> Bp = (gptr<TB>)T.B;
     gptr_mut<TC> Cp = (gptr_mut<TC>)T.C;
-    const int m0 = (blk % bmc) * BM, n0 = (blk / bmc) * BN;
+    const int m0 = (blk % bmc) * TBM, n0 = (blk / bmc) * TBN;
     const int t = threadIdx.x, l = t % 64, w = t / 64;
-    const int wm = w / 2, wn = w % 2;
+    const int wm = w % WMW, wn = w / WMW;
     typedef typename AccT<CT>::type Acc;
     Acc acc[4][4];
 #pragma unroll
@@ -521,6 +530,24 @@ static int try_typed(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
                      bool fast, int64_t grid, int bmc, int bnc, int xcd, unsigned long long* fl) {
     if (one.ta != DtOf<TA>::v || one.tb != DtOf<TB>::v || one.tc != DtOf<TC>::v) return 0;
     if (one.transA != TRA || (one.transB != 0) != (TRB != 0)) return 0;
+    if constexpr (sizeof(CT) == 2 && ROLE == GEMM_TRMM && TRA == 1 && TRB == 0) {
+        int choice = g_f16_grid;
+        if (choice < 0)
+            choice = (one.N % 256 == 0 && (int64_t)ntasks * (one.M / 128) * (one.N / 256) >= 2048) ? 2 : 0;
+        if (fast && choice != 0 && one.M % 256 == 0 && one.N % 256 == 0) {
+            const bool tall = choice == 1;   // 1: 4 x 2 waves (256 x 128), 2: 2 x 4 waves (128 x 256)
+            const int bm = tall ? 256 : 128, bn = tall ? 128 : 256;
+            const int bmc2 = one.M / bm, bnc2 = one.N / bn, bpt2 = bmc2 * bnc2;
+            int64_t grid2 = xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt2 : (int64_t)ntasks * bpt2;
+            if (tall)
+                hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 4, 2>), dim3((unsigned)grid2),
+                                   dim3(512), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
+            else
+                hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4>), dim3((unsigned)grid2),
+                                   dim3(512), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
+            return 1;
+        }
+    }
     if (fast)
         hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE>), dim3((unsigned)grid), dim3(NTHR), 0, s,
                            d_tasks, one, ntasks, bmc, bnc, xcd, fl);
@@ -548,8 +575,8 @@ static int launch_ct(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
     if (grid > 0x7fffffffLL) return set_err(ctx, GPEX_ERR_ARG, "gemm grid too large");
     unsigned long long* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
     // typed fast kernels for the operand-type combinations of the hot launches
-    bool tfast = (M % BM == 0) && (N % BN == 0) && (K % TCfg<CT>::BK == 0) && (one.lda % 4 == 0) &&
-                 (one.ldb % 4 == 0) && al(one.A) && al(one.B);
+    bool tfast = (M % BM == 0) && (N % BN == 0) && (K % TCfg<CT>::BK == 0) && (one.lda % 8 == 0) &&
+                 (one.ldb % 8 == 0) && al(one.A) && al(one.B);
     // NT form (trailing updates, panel solves) and NN form (TRMM) with uniform or TRMM/TRSM types
     int done = try_typed<CT, CT, CT, CT, 0, 1, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
     if (!done) done = try_typed<CT, CT, CT, CT, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
