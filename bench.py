@@ -41,9 +41,7 @@ def tile_flops(pmap, nt, nb, nsim, amp):
     nb3 = float(nb) ** 3
     for k in range(nt):
         f["fp64"] += nb3 / 3.0                                   # POTRF of the diagonal tile
-        for i in range(k + 1, nt):
-            p = int(pmap[i, k])
-            f["fp64" if p == 0 else "fp32"] += nb3               # panel solve (FP16 computed in FP32)
+        f["fp64"] += (nt - k - 1) * nb3                          # panel solves, FP64 for every tile
         for j in range(k + 1, nt):
             f["fp64"] += nb3                                     # SYRK of diagonal tile j
             for i in range(j + 1, nt):
