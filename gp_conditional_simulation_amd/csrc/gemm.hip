@@ -19,6 +19,7 @@
 //   * The next K slab is prefetched into registers while the current one is multiplied.
 //   * Batched launches place all workgroups of one task on one XCD (workgroups are dealt to the
 //     8 XCDs round-robin by index), so a task's operand tiles stream through a single L2.
+#include <type_traits>
 #include "common.h"
 #include "devutil.h"
 
@@ -34,6 +35,8 @@ constexpr int BM = 128, BN = 128, NTHR = 256;
 // Wave grid of FP16 TRMM launches: -1 = chosen per launch (2 x 4 waves when that still gives at
 // least 2048 workgroups, else 2 x 2), 0 = 2 x 2 waves (128 x 128), 1 = 4 x 2, 2 = 2 x 4.
 int g_f16_grid = -1;
+int g_f64_wide = 0;
+int g_f64_waves4 = 0;
 
 template <typename CT> struct Cfg;
 template <> struct Cfg<double> { static constexpr int BK = 16, PAD = 2; };
@@ -149,6 +152,10 @@ __device__ __forceinline__ void mma(f4& c, float a, float b) {
 __device__ __forceinline__ void mma(f4& c, h8 a, h8 b) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+
+// Register fragment of one matrix-core step: one element per lane (FP64/FP32), 8 (FP16).
+template <typename CT> struct FragT { typedef CT type; };
+template <> struct FragT<_Float16> { typedef h8 type; };
 
 // Row of accumulator element r held by lane l inside a 16 x 16 matrix-core tile.
 template <typename CT> __device__ __forceinline__ int acc_row(int l, int r) { return 4 * (l / 16) + r; }
@@ -326,63 +333,77 @@ struct TSlab {
 
     __device__ __forceinline__ static int idx(int row, int k) { return KROW ? k * LDR + row : row * LDK + k; }
 
+    // Vector q of this thread's share of the slab at (r0, k0), from global memory into registers.
+    __device__ __forceinline__ void load_q(int q, gptr<T> base, int64_t ld, int r0, int k0, int R, int K, int t) {
+        int r, k;
+        if (CR) {
+            r = (t % TPK) * VE;
+            k = t / TPK + (THREADS / TPK) * q;
+        } else {
+            constexpr int TPR = BK / VE;
+            r = t / TPR + (THREADS / TPR) * q;
+            k = (t % TPR) * VE;
+        }
+        int gr = r0 + r, gk = k0 + k;
+        if (!EDGE) {
+            int64_t id = CR ? (int64_t)gr + (int64_t)gk * ld : (int64_t)gk + (int64_t)gr * ld;
+            typedef typename VN<T, VE>::type VT;
+            VT x = *reinterpret_cast<const __attribute__((address_space(1))) VT*>(base + id);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) v[q][e] = to_ct<CT, T>(x[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                int rr = CR ? gr + e : gr;
+                int kk = CR ? gk : gk + e;
+                v[q][e] = (rr < R && kk < K)
+                              ? to_ct<CT, T>(base[CR ? (int64_t)rr + (int64_t)kk * ld : (int64_t)kk + (int64_t)rr * ld])
+                              : CT(0);
+            }
+        }
+    }
+
     __device__ __forceinline__ void load(gptr<T> base, int64_t ld, int r0, int k0, int R, int K, int t) {
 #pragma unroll
-        for (int q = 0; q < VPT; ++q) {
-            int r, k;
-            if (CR) {
-                r = (t % TPK) * VE;
-                k = t / TPK + (THREADS / TPK) * q;
-            } else {
-                constexpr int TPR = BK / VE;
-                r = t / TPR + (THREADS / TPR) * q;
-                k = (t % TPR) * VE;
-            }
-            int gr = r0 + r, gk = k0 + k;
-            if (!EDGE) {
-                int64_t id = CR ? (int64_t)gr + (int64_t)gk * ld : (int64_t)gk + (int64_t)gr * ld;
-                typedef typename VN<T, VE>::type VT;
-                VT x = *reinterpret_cast<const __attribute__((address_space(1))) VT*>(base + id);
+        for (int q = 0; q < VPT; ++q) load_q(q, base, ld, r0, k0, R, K, t);
+    }
+
+    // Vector q of the registers into the LDS slab.
+    __device__ __forceinline__ void store_q(int q, CT* sm, int t) {
+        if (CR) {
+            int r = (t % TPK) * VE, k = t / TPK + (THREADS / TPK) * q;
 #pragma unroll
-                for (int e = 0; e < VE; ++e) v[q][e] = to_ct<CT, T>(x[e]);
-            } else {
+            for (int e = 0; e < VE; ++e) sm[idx(r + e, k)] = v[q][e];
+        } else {
+            constexpr int TPR = BK / VE;
+            int r = t / TPR + (THREADS / TPR) * q, k = (t % TPR) * VE;
 #pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    int rr = CR ? gr + e : gr;
-                    int kk = CR ? gk : gk + e;
-                    v[q][e] = (rr < R && kk < K)
-                                  ? to_ct<CT, T>(base[CR ? (int64_t)rr + (int64_t)kk * ld : (int64_t)kk + (int64_t)rr * ld])
-                                  : CT(0);
-                }
-            }
+            for (int e = 0; e < VE; ++e) sm[idx(r, k + e)] = v[q][e];
         }
     }
 
     __device__ __forceinline__ void store(CT* sm, int t) {
 #pragma unroll
-        for (int q = 0; q < VPT; ++q) {
-            if (CR) {
-                int r = (t % TPK) * VE, k = t / TPK + (THREADS / TPK) * q;
-#pragma unroll
-                for (int e = 0; e < VE; ++e) sm[idx(r + e, k)] = v[q][e];
-            } else {
-                constexpr int TPR = BK / VE;
-                int r = t / TPR + (THREADS / TPR) * q, k = (t % TPR) * VE;
-#pragma unroll
-                for (int e = 0; e < VE; ++e) sm[idx(r, k + e)] = v[q][e];
-            }
-        }
+        for (int q = 0; q < VPT; ++q) store_q(q, sm, t);
     }
 };
 
-// WMW x WNW waves of 64 x 64 each: a block of (64 WMW) x (64 WNW) outputs per workgroup.
+// Waves resident per SIMD for a wave tile of 64 x (16 FJ).
+template <int FJ> struct WavesPerEU { static constexpr int v = FJ == 8 ? 1 : FJ == 2 ? 4 : 2; };
+
+// WMW x WNW waves of 64 x (16 FJ) each: a block of (64 WMW) x (16 FJ WNW) outputs per workgroup.
+// FJ = 4: 64 x 64 per wave, two waves per SIMD.  FJ = 2: 64 x 32 per wave, four waves per SIMD
+// (a single wave issues FP64 matrix-core ops at only about half the pipe's rate, so the more
+// waves are ready to issue, the less a stalled one costs).  FJ = 8: 64 x 128 per wave, its 128
+// FP64 accumulators filling the accumulation registers, one wave per SIMD.
 template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, bool EDGE, int ROLE,
-          int WMW = 2, int WNW = 2>
-__global__ __launch_bounds__(64 * WMW * WNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+          int WMW = 2, int WNW = 2, int FJ = 4>
+__global__ __launch_bounds__(64 * WMW * WNW)
+__attribute__((amdgpu_waves_per_eu(WavesPerEU<FJ>::v, WavesPerEU<FJ>::v)))
 void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int bmc, int bnc, int xcd_map,
               unsigned long long* flags) {
     constexpr int BK = TCfg<CT>::BK;
-    constexpr int TBM = 64 * WMW, TBN = 64 * WNW, THR = 64 * WMW * WNW;
+    constexpr int TBM = 64 * WMW, WTN = 16 * FJ, TBN = WTN * WNW, THR = 64 * WMW * WNW;
     constexpr bool a_contig_r = TRA == 0;
     constexpr bool b_contig_r = TRB != 0;
     typedef TSlab<CT, TA, a_contig_r, EDGE, TBM, THR> SA;
@@ -416,100 +437,164 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     const int t = threadIdx.x, l = t % 64, w = t / 64;
     const int wm = w % WMW, wn = w / WMW;
     typedef typename AccT<CT>::type Acc;
-    Acc acc[4][4];
+    // With FJ = 8 the accumulators live in the accumulation registers; zeroing them with a
+    // matrix-core op (rather than vector moves) keeps the loop-carried values in that register
+    // class, where the compiler otherwise shuttles them through the vector registers every slab.
+    Acc acc[4][FJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+        for (int j = 0; j < FJ; ++j) {
+            acc[i][j] = Acc{0, 0, 0, 0};
+            if constexpr (FJ == 8) {
+                if constexpr (sizeof(CT) == 2) mma(acc[i][j], h8{}, h8{});
+                else mma(acc[i][j], (CT)0, (CT)0);
+            }
+        }
 
     SA la;
     SB lb;
     const int nk = (T.K + BK - 1) / BK;
+    // Operand slabs are prefetched two ahead: slab 0 goes to LDS and slab 1 stays in registers;
+    // during slab kb each register vector is stored into the other LDS buffer (slab kb + 1) and
+    // then reloaded from global memory with slab kb + 2, spread over the slab's steps.
     la.load(Ap, T.lda, m0, 0, T.M, T.K, t);
     lb.load(Bp, T.ldb, n0, 0, T.N, T.K, t);
     la.store(As[0], t);
     lb.store(Bs[0], t);
-    __syncthreads();
-    for (int kb = 0; kb < nk; ++kb) {
-        const int cur = kb & 1;
-        if (kb + 1 < nk) {
-            la.load(Ap, T.lda, m0, (kb + 1) * BK, T.M, T.K, t);
-            lb.load(Bp, T.ldb, n0, (kb + 1) * BK, T.N, T.K, t);
-        }
-        const CT* as = As[cur];
-        const CT* bs = Bs[cur];
-        if constexpr (sizeof(CT) == 2) {
-#pragma unroll
-            for (int ks = 0; ks < BK; ks += 32) {
-                h8 af[4], bf[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    af[i] = *reinterpret_cast<const h8*>(&as[SA::idx(wm * 64 + i * 16 + l % 16, ks + 8 * (l / 16))]);
-                    bf[i] = *reinterpret_cast<const h8*>(&bs[SB::idx(wn * 64 + i * 16 + l % 16, ks + 8 * (l / 16))]);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) mma(acc[i][j], af[i], bf[j]);
-            }
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < BK; ks += 16) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    CT af[4], bf[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        af[i] = as[SA::idx(wm * 64 + i * 16 + l % 16, ks + 4 * (l / 16) + e)];
-                        bf[i] = bs[SB::idx(wn * 64 + i * 16 + l % 16, ks + 4 * (l / 16) + e)];
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) mma(acc[i][j], af[i], bf[j]);
-                }
-            }
-        }
-        if (kb + 1 < nk) {
-            la.store(As[cur ^ 1], t);
-            lb.store(Bs[cur ^ 1], t);
-        }
-        __syncthreads();
+    if (nk > 1) {
+        la.load(Ap, T.lda, m0, BK, T.M, T.K, t);
+        lb.load(Bp, T.ldb, n0, BK, T.N, T.K, t);
     }
+    __syncthreads();
 
+    // Matrix-core steps: 4 k per step for FP64/FP32 (lane group g supplies k = 4 g + e of a 16-k
+    // group), 32 k per step for FP16 (8 consecutive k per lane group).  Fragments are double
+    // buffered in registers: step st + 1 is read from LDS while step st's products run, and at the
+    // end of a slab the next slab's first fragments are read right after the barrier, before the
+    // slab's last products, so the barrier wait does not drain the matrix-core pipe.
+    constexpr int KST = sizeof(CT) == 2 ? 32 : 4;
+    constexpr int NST = BK / KST;
+    static_assert(NST % 2 == 0, "the register double buffer needs an even step count per slab");
+    constexpr int NV = SA::VPT + SB::VPT;   // register vectors per thread per slab
+    typedef typename FragT<CT>::type FT;
+    FT fa[2][4], fb[2][FJ];
+    auto rd = [&](const CT* as, const CT* bs, int st, FT* af, FT* bf) {
+        if constexpr (sizeof(CT) == 2) {
+            const int ks = st * 32;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                af[i] = *reinterpret_cast<const h8*>(&as[SA::idx(wm * 64 + i * 16 + l % 16, ks + 8 * (l / 16))]);
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+                bf[j] = *reinterpret_cast<const h8*>(&bs[SB::idx(wn * WTN + j * 16 + l % 16, ks + 8 * (l / 16))]);
+        } else {
+            const int kk = (st / 4) * 16 + 4 * (l / 16) + st % 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = as[SA::idx(wm * 64 + i * 16 + l % 16, kk)];
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) bf[j] = bs[SB::idx(wn * WTN + j * 16 + l % 16, kk)];
+        }
+    };
+
+    // One slab.  WR: slab kb + 1 exists (its registers are stored and the barrier is taken);
+    // LD: slab kb + 2 exists (reloaded into the freed registers).  The last two slabs are peeled
+    // off so that every path is straight-line code: the compiler's wait counts then let the
+    // deferred products run while the new fragments are in flight.  Scheduling fences keep the
+    // order per step: next fragments' LDS reads, this step's share of the register vectors
+    // (store, reload), the products; in the last step the barrier and the next slab's first reads
+    // come ahead of the deferred products.
+    auto slab = [&](int kb, auto wr_t, auto ld_t) {
+        constexpr bool WR = decltype(wr_t)::value;
+        constexpr bool LD = decltype(ld_t)::value;
+        const int cur = kb & 1;
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            const int p = st & 1, q = p ^ 1;
+            if (st + 1 < NST) {
+                rd(As[cur], Bs[cur], st + 1, fa[q], fb[q]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (WR) {
+                // this step's share of the vectors, spread over all but the last step
+#pragma unroll
+                for (int vq = 0; vq < NV; ++vq) {
+                    if (vq * (NST - 1) / NV != st) continue;
+                    if (vq < SA::VPT) {
+                        la.store_q(vq, As[cur ^ 1], t);
+                        if constexpr (LD) la.load_q(vq, Ap, T.lda, m0, (kb + 2) * BK, T.M, T.K, t);
+                    } else {
+                        lb.store_q(vq - SA::VPT, Bs[cur ^ 1], t);
+                        if constexpr (LD) lb.load_q(vq - SA::VPT, Bp, T.ldb, n0, (kb + 2) * BK, T.N, T.K, t);
+                    }
+                }
+                if (st + 1 == NST) {
+                    __syncthreads();
+                    rd(As[cur ^ 1], Bs[cur ^ 1], 0, fa[q], fb[q]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) mma(acc[i][j], fb[p][j], fa[p][i]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    rd(As[0], Bs[0], 0, fa[0], fb[0]);
+    for (int kb = 0; kb + 2 < nk; ++kb) slab(kb, std::true_type{}, std::true_type{});
+    if (nk >= 2) slab(nk - 2, std::true_type{}, std::false_type{});
+    slab(nk - 1, std::false_type{}, std::false_type{});
+
+    // Epilogue.  The operands went into the matrix cores as (B, A), so fragment (i, j) holds the
+    // transposed 16 x 16 block: lane l is row l % 16 and register r is column acc_row(l, r).  The 16
+    // lanes of a column then cover 16 consecutive rows of the column-major C (whole cache lines), and
+    // each row group's old C values are all loaded before any store, so their latencies overlap.
     bool ovf = false;
     _Float16* __restrict__ C2 = T.C2;
+    const bool use_beta = T.beta != 0.0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        const int row = m0 + wm * 64 + i * 16 + l % 16;
+        TC cold[FJ][4];
+        if (use_beta) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int col = n0 + wn * WTN + j * 16 + acc_row<CT>(l, r);
+                    cold[j][r] = (!EDGE || (row < T.M && col < T.N)) ? Cp[(int64_t)row + (int64_t)col * T.ldc]
+                                                                     : TC(0);
+                }
+        }
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                int row = m0 + wm * 64 + i * 16 + acc_row<CT>(l, r);
-                int col = n0 + wn * 64 + j * 16 + l % 16;
+                const int col = n0 + wn * WTN + j * 16 + acc_row<CT>(l, r);
                 if (EDGE && (row >= T.M || col >= T.N)) continue;
-                int64_t ci = (int64_t)row + (int64_t)col * T.ldc;
+                const int64_t ci = (int64_t)row + (int64_t)col * T.ldc;
                 double sv;   // the stored value, exactly, for the optional FP16 copy
                 if constexpr (sizeof(TC) == 8) {
                     double v = T.alpha * (double)acc[i][j][r];
-                    if (T.beta != 0.0) v += T.beta * (double)Cp[ci];
+                    if (use_beta) v += T.beta * (double)cold[j][r];
                     Cp[ci] = v;
                     sv = v;
                 } else if constexpr (sizeof(TC) == 4) {
                     float v = (float)T.alpha * (float)acc[i][j][r];
-                    if (T.beta != 0.0) v += (float)T.beta * (float)Cp[ci];
+                    if (use_beta) v += (float)T.beta * (float)cold[j][r];
                     Cp[ci] = v;
                     sv = (double)v;
                 } else if constexpr (sizeof(CT) == 8) {
                     double v = T.alpha * acc[i][j][r];
-                    if (T.beta != 0.0) v += T.beta * (double)Cp[ci];
+                    if (use_beta) v += T.beta * (double)cold[j][r];
                     _Float16 h = f64_to_f16(v);
                     if (__builtin_isinf((float)h) && !__builtin_isinf(v)) ovf = true;
                     Cp[ci] = h;
                     sv = (double)h;
                 } else {
                     float v = (float)T.alpha * (float)acc[i][j][r];
-                    if (T.beta != 0.0) v += (float)T.beta * (float)Cp[ci];
+                    if (use_beta) v += (float)T.beta * (float)cold[j][r];
                     _Float16 h = (_Float16)v;
                     if (__builtin_isinf((float)h) && !__builtin_isinf(v)) ovf = true;
                     Cp[ci] = h;
@@ -521,6 +606,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
                     if (__builtin_isinf((float)h2) && !__builtin_isinf(sv)) ovf = true;
                 }
             }
+    }
     if (ovf && flags) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
 }
 
@@ -545,6 +631,24 @@ static int try_typed(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
             else
                 hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4>), dim3((unsigned)grid2),
                                    dim3(512), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
+            return 1;
+        }
+    }
+    if constexpr (sizeof(CT) == 8) {
+        if (fast && g_f64_waves4) {
+            // 128 x 128 blocks of eight 64 x 32 waves, two blocks per CU: four waves per SIMD
+            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4, 2>), dim3((unsigned)grid),
+                               dim3(512), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+            return 1;
+        }
+        // 128 x 256 blocks of four 64 x 128 waves when the launch still fills the chip twice over
+        int wide = g_f64_wide;
+        if (wide < 0) wide = (int64_t)ntasks * (one.M / 128) * (one.N / 256) >= 512;
+        if (fast && wide && one.M % 128 == 0 && one.N % 256 == 0) {
+            const int bmc2 = one.M / 128, bnc2 = one.N / 256, bpt2 = bmc2 * bnc2;
+            int64_t grid2 = xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt2 : (int64_t)ntasks * bpt2;
+            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 2, 8>), dim3((unsigned)grid2),
+                               dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
             return 1;
         }
     }
