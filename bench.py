@@ -14,7 +14,7 @@ Phase times come from HIP events on the library's stream; the dominant kernel's 
 the library's own per-launch events.  The CPU baseline times the oracle on a bounded leading
 block of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--trmm-sweep]
 """
 import argparse
 import json
@@ -55,6 +55,19 @@ def tile_flops(pmap, nt, nb, nsim, amp):
     return f
 
 
+def hbm_rates(info, n, nsim, t_gen_ms, t_scan_ms):
+    """Phase-level HBM rates: covariance tiles written by the generator (each lower tile in its
+    storage precision; the phase also holds the statistics pass and the host plan) and the S
+    entries read by the scan (the phase also holds the host quantile step)."""
+    esz = {0: 8, 1: 4, 2: 2}
+    pm, nt, nb = info["map"], info["nt"], info["nb"]
+    wbytes = sum(esz[int(pm[i, j])] for i in range(nt) for j in range(i + 1)) * float(nb) * nb
+    rbytes = float(n) * nsim * 8
+    return {"cov_gen": {"bytes_written": wbytes, "GB_per_s": round(wbytes / (t_gen_ms * 1e-3) / 1e9, 1)},
+            "scan": {"bytes_read": rbytes, "GB_per_s": round(rbytes / (t_scan_ms * 1e-3) / 1e9, 1)},
+            "peak_GB_per_s": HBM_GBS}
+
+
 def traffic_per_launch(prec):
     """HBM bytes per trailing-update launch from the committed counter summary, if it was taken
     on the current GEMM source (else None)."""
@@ -92,21 +105,85 @@ def cpu_baseline(w, rows):
                       f"(covariance {t1 - t0:.2f} s, normals {t3 - t2:.2f} s not counted), info {info}"}
 
 
+SWEEP_N = (16384, 32768, 65536, 98304, 131072)
+SWEEP_BETA = (("weak", 0.033), ("medium", 0.1), ("strong", 0.234))
+
+
+def trmm_sweep(args):
+    """Single-GPU TRMM throughput against N at three correlation levels, after the shape of the
+    pages' single-node TRMM figure ("Mixed-Precision GPU Acceleration for Confidence Regions of
+    Spatial Excursion Sets", Fig. 6): N uniform locations (Morton order), Matern nu = 1/2,
+    sigma^2 = 1, nugget 1e-4, range 0.033 / 0.1 / 0.234, tile 1024, tolerance 1e-8, nsim columns.
+    The factor is computed once per point; the TRMM (seeded normals, B = Z/s in FP16, FP32
+    diagonal, FP16 off-diagonal, FP64 output) is timed over three runs after a warm-up.  Reported
+    as N^2 nsim / T and as a multiple of the FP64 matrix-core peak."""
+    import numpy as np
+    import torch
+
+    import gp_conditional_simulation_amd as g
+    import gpex_synth as syn
+
+    dev = torch.device("cuda:0")
+    ctx = g.Context(0)
+    nsim, nb = args.sweep_nsim, 1024
+    sizes = [n for n in SWEEP_N if n <= args.sweep_max_n]
+    rows = []
+    for n in sizes:
+        x, y = syn.uniform_locations(n, 1005)
+        x, y, _ = syn.ordered_locations(x, y)
+        loc = torch.tensor(np.r_[x, y], dtype=torch.float64, device=dev)
+        M = g.colmajor(n, nsim, ctx)
+        for level, beta in SWEEP_BETA:
+            params = {"kind": 0, "sigma2": 1.0, "range": beta, "nu": 0.5, "nugget": 1e-4}
+            A = g.cov_gen(ctx, loc, n, params, nb, amp=1, tol=1e-8)
+            info = g.potrf_mp(ctx, A)
+            if info != 0:
+                raise RuntimeError(f"factorisation failed at column {info} (N={n}, range {beta})")
+            times = []
+            for r in range(4):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                g.trmm_sim(ctx, A, nsim, seed=2005, M=M, want_diag=False)
+                e1.record()
+                torch.cuda.synchronize()
+                if r:
+                    times.append(e0.elapsed_time(e1))
+            t = statistics.median(times)
+            tf = float(n) ** 2 * nsim / (t * 1e-3) / 1e12
+            rows.append({"n": n, "correlation": level, "range": beta, "tiles_fp64_fp32_fp16": A.diag["tiles"],
+                         "trmm_ms": round(t, 3), "tflops": round(tf, 1),
+                         "x_fp64_peak": round(tf / PEAK_TF["fp64"], 2)})
+            log(f"N {n} {level}: trmm {t:.2f} ms  {tf:.1f} Tflop/s  {tf / PEAK_TF['fp64']:.2f}x FP64 peak")
+            A.close()
+        del M, loc
+        torch.cuda.empty_cache()
+    best = {lv: max(r["x_fp64_peak"] for r in rows if r["correlation"] == lv) for lv, _ in SWEEP_BETA}
+    print(json.dumps({"metric": "single-GPU TRMM Tflop/s vs N (N^2 nsim / T_trmm)", "nsim": nsim, "nb": nb,
+                      "fp64_peak_tflops": PEAK_TF["fp64"], "max_x_fp64_peak": best, "points": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="unif100k_tol1e-8")
     ap.add_argument("--cpu-rows", type=int, default=10240)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
+    ap.add_argument("--trmm-sweep", action="store_true",
+                    help="TRMM throughput against N at three correlation levels instead of the step benchmark")
+    ap.add_argument("--sweep-nsim", type=int, default=2048)
+    ap.add_argument("--sweep-max-n", type=int, default=131072)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library's path is single-device (use --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+    if args.trmm_sweep:
+        trmm_sweep(args)
+        return
 
     import numpy as np
     import torch
@@ -168,6 +245,8 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     med = lambda k: statistics.median(r[k] for r in recs)   # noqa: E731
+    lo = lambda k: min(r[k] for r in recs)                   # noqa: E731
+    hi = lambda k: max(r[k] for r in recs)                   # noqa: E731
     T_potrf, T_trmm, T_scan, T_gen = med("potrf"), med("trmm"), med("scan"), med("gen")
     N, nsim = w.n, w.nsim
     flops = N ** 3 / 3.0 + float(N) ** 2 * nsim
@@ -200,12 +279,17 @@ def main():
         "sims_per_s_end_to_end": round(nsim / (ms_per_step * 1e-3), 1),
         "phase_ms_median": {"cov_gen": round(T_gen, 2), "potrf": round(T_potrf, 2), "trmm": round(T_trmm, 2),
                             "scan": round(T_scan, 2)},
+        "phase_ms_min": {k: round(lo(r), 2) for k, r in (("cov_gen", "gen"), ("potrf", "potrf"), ("trmm", "trmm"),
+                                                         ("scan", "scan"))},
+        "phase_ms_max": {k: round(hi(r), 2) for k, r in (("cov_gen", "gen"), ("potrf", "potrf"), ("trmm", "trmm"),
+                                                         ("scan", "scan"))},
+        "hbm_phase_rates": hbm_rates(info, N, nsim, T_gen, T_scan),
         "precision_weighted_roofline": {"ideal_ms": round(t_ideal * 1e3, 2),
                                         "frac": round(t_ideal / ((T_potrf + T_trmm) * 1e-3), 4),
                                         "flops": {k: float(f"{v:.4e}") for k, v in tf.items()}},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TF[prec], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TF[prec], 4), "traffic": traffic_per_launch(prec),
-                     "kernel": "gpex::k_gemm_t<{0}, {0}, {0}, {0}, 0, 1, false, 1> (trailing tile update, {1})".format(
+                     "kernel": "gpex::k_gemm_t<{0}, {0}, {0}, {0}, 0, 1, false, 1, 2, 2, 4, 1> (trailing tile update, {1})".format(
                          {"fp64": "double", "fp32": "float", "fp16": "_Float16"}[prec], prec),
                      "launches": launches, "avg_launch_ms": round(per_launch_ms, 4),
                      "flops_per_launch": float(f"{per_launch_flops:.4e}")},

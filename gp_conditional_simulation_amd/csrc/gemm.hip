@@ -37,6 +37,7 @@ constexpr int BM = 128, BN = 128, NTHR = 256;
 int g_f16_grid = -1;
 int g_f64_wide = 0;
 int g_f64_waves4 = 0;
+int g_gemm_interleave = 1;
 
 template <typename CT> struct Cfg;
 template <> struct Cfg<double> { static constexpr int BK = 16, PAD = 2; };
@@ -397,7 +398,7 @@ template <int FJ> struct WavesPerEU { static constexpr int v = FJ == 8 ? 1 : FJ 
 // waves are ready to issue, the less a stalled one costs).  FJ = 8: 64 x 128 per wave, its 128
 // FP64 accumulators filling the accumulation registers, one wave per SIMD.
 template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, bool EDGE, int ROLE,
-          int WMW = 2, int WNW = 2, int FJ = 4>
+          int WMW = 2, int WNW = 2, int FJ = 4, int INTERLEAVE = 0>
 __global__ __launch_bounds__(64 * WMW * WNW)
 __attribute__((amdgpu_waves_per_eu(WavesPerEU<FJ>::v, WavesPerEU<FJ>::v)))
 void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int bmc, int bnc, int xcd_map,
@@ -477,6 +478,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     constexpr int NST = BK / KST;
     static_assert(NST % 2 == 0, "the register double buffer needs an even step count per slab");
     constexpr int NV = SA::VPT + SB::VPT;   // register vectors per thread per slab
+    constexpr bool IL = INTERLEAVE != 0;
     typedef typename FragT<CT>::type FT;
     FT fa[2][4], fb[2][FJ];
     auto rd = [&](const CT* as, const CT* bs, int st, FT* af, FT* bf) {
@@ -513,7 +515,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
             const int p = st & 1, q = p ^ 1;
             if (st + 1 < NST) {
                 rd(As[cur], Bs[cur], st + 1, fa[q], fb[q]);
-                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (WR) {
                 // this step's share of the vectors, spread over all but the last step
@@ -538,6 +540,15 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < FJ; ++j) mma(acc[i][j], fb[p][j], fa[p][i]);
+            if constexpr (IL) {
+                // one product, then one LDS or global-memory instruction, in turn
+#pragma unroll
+                for (int g = 0; g < 12; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x0A0, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * FJ, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -625,8 +636,14 @@ static int try_typed(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
             const int bm = tall ? 256 : 128, bn = tall ? 128 : 256;
             const int bmc2 = one.M / bm, bnc2 = one.N / bn, bpt2 = bmc2 * bnc2;
             int64_t grid2 = xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt2 : (int64_t)ntasks * bpt2;
-            if (tall)
+            if (tall && g_gemm_interleave)
+                hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 4, 2, 4, 1>), dim3((unsigned)grid2),
+                                   dim3(512), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
+            else if (tall)
                 hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 4, 2>), dim3((unsigned)grid2),
+                                   dim3(512), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
+            else if (g_gemm_interleave)
+                hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4, 4, 1>), dim3((unsigned)grid2),
                                    dim3(512), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
             else
                 hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4>), dim3((unsigned)grid2),
@@ -652,7 +669,10 @@ static int try_typed(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
             return 1;
         }
     }
-    if (fast)
+    if (fast && g_gemm_interleave)
+        hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 2, 4, 1>), dim3((unsigned)grid),
+                           dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+    else if (fast)
         hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE>), dim3((unsigned)grid), dim3(NTHR), 0, s,
                            d_tasks, one, ntasks, bmc, bnc, xcd, fl);
     else
