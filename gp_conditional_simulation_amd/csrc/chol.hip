@@ -153,23 +153,23 @@ int potrf_inv(gpex_ctx_t ctx, hipStream_t s, double* A, int64_t lda, double* T, 
     double* T21 = T + n1;
     double* T22 = T + n1 + (int64_t)n1 * ldt;
     auto g = [&](const void* a, int tA, int64_t la, const void* b, int tB, int64_t lb, void* c,
-                 int64_t lc, int M, int N, int K, double al, double be) {
+                 int64_t lc, int M, int N, int K, double al, double be, int tri) {
         GemmTask t{};
         t.A = a; t.B = b; t.C = c; t.lda = la; t.ldb = lb; t.ldc = lc;
         t.M = M; t.N = N; t.K = K; t.ta = DT_F64; t.tb = DT_F64; t.tc = DT_F64;
-        t.transA = (int8_t)tA; t.transB = (int8_t)tB; t.alpha = al; t.beta = be;
+        t.transA = (int8_t)tA; t.transB = (int8_t)tB; t.alpha = al; t.beta = be; t.tri = (int8_t)tri;
         return gemm_launch(ctx, s, DT_F64, nullptr, 1, t);
     };
     GPEX_TRY(potrf_inv(ctx, s, A, lda, T, ldt, n1, ws, col0));
-    // L21 = A21 T11^T (through ws: the product must not overwrite its own input)
-    GPEX_TRY(g(A21, 0, lda, T, 1, ldt, ws, n2, n2, n1, n1, 1.0, 0.0));
+    // L21 = A21 T11^T (through ws: the product must not overwrite its own input); T11^T is upper
+    GPEX_TRY(g(A21, 0, lda, T, 1, ldt, ws, n2, n2, n1, n1, 1.0, 0.0, TRI_B_UPPER));
     GPEX_TRY(copy2d(ctx, s, ws, DT_F64, n2, A21, DT_F64, lda, n2, n1, 1.0));
-    // A22 -= L21 L21^T
-    GPEX_TRY(g(A21, 0, lda, A21, 1, lda, A22, lda, n2, n2, n1, -1.0, 1.0));
+    // A22 -= L21 L21^T (only its lower triangle is used)
+    GPEX_TRY(g(A21, 0, lda, A21, 1, lda, A22, lda, n2, n2, n1, -1.0, 1.0, TRI_C_LOWER));
     GPEX_TRY(potrf_inv(ctx, s, A22, lda, T22, ldt, n2, ws, col0 + n1));
-    // T21 = -T22 (L21 T11)
-    GPEX_TRY(g(A21, 0, lda, T, 0, ldt, ws, n2, n2, n1, n1, 1.0, 0.0));
-    GPEX_TRY(g(T22, 0, ldt, ws, 0, n2, T21, ldt, n2, n1, n2, -1.0, 0.0));
+    // T21 = -T22 (L21 T11); T22 is lower
+    GPEX_TRY(g(A21, 0, lda, T, 0, ldt, ws, n2, n2, n1, n1, 1.0, 0.0, 0));
+    GPEX_TRY(g(T22, 0, ldt, ws, 0, n2, T21, ldt, n2, n1, n2, -1.0, 0.0, TRI_A_LOWER));
     // upper-right blocks of the factor and of its inverse are zero
     GPEX_TRY(zero2d(ctx, s, A + (int64_t)n1 * lda, lda, n1, n2));
     GPEX_TRY(zero2d(ctx, s, T + (int64_t)n1 * ldt, ldt, n1, n2));
@@ -257,6 +257,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             g.ta = (int8_t)p; g.tb = DT_F64; g.tc = (int8_t)p;
             g.transA = 0; g.transB = 1;
             g.alpha = 1.0; g.beta = 0.0;
+            g.tri = TRI_B_UPPER;   // T_kk^T is upper triangular
             if (a->l16) {   // tile (i, k) lands at columns [k nb, (k+1) nb) of row panel i
                 g.C2 = a->l16_panel(i) + (size_t)k * nb;
                 g.ldc2 = i * nb;
@@ -275,6 +276,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
                 g.ta = (int8_t)a->prec(i, k); g.tb = (int8_t)a->prec(j, k); g.tc = (int8_t)p;
                 g.transA = 0; g.transB = 1;
                 g.alpha = -1.0; g.beta = 1.0;
+                g.tri = (i == j) ? TRI_C_LOWER : 0;   // diagonal tiles: only the lower triangle is used
                 (j == k + 1 ? update_next : update)[sig(p, g)].push_back(g);
                 upd_flops[(size_t)p] += (i == j ? 1.0 : 2.0) * nb * (double)nb * nb;
             }

@@ -86,13 +86,22 @@ struct GemmTask {
     void* C;
     int64_t lda, ldb, ldc;
     int M, N, K;
-    int8_t ta, tb, tc, transA, transB, pad0, pad1, pad2;
+    int8_t ta, tb, tc, transA, transB;
+    int8_t tri;   // TRI_* flags: triangular structure the kernels may exploit (results are unchanged)
+    int8_t pad1, pad2;
     double alpha, beta;
     // Optional second output (typed kernels only): the stored result converted to FP16 and
     // written row-major, element (row, col) at C2[col + row * ldc2].
     _Float16* C2;
     int64_t ldc2;
 };
+
+// Triangular structure of a task.  TRI_C_LOWER: only the lower triangle of C is wanted (blocks
+// strictly above the diagonal are skipped and keep their old contents).  TRI_A_LOWER: op(A) is
+// lower triangular (zero for k > row), so a block of rows stops its K loop after its last row.
+// TRI_B_UPPER: op(B) is upper triangular (zero for k > column), so a block of columns stops after
+// its last column.  The skipped products are exact zeros.
+enum : int { TRI_C_LOWER = 1, TRI_A_LOWER = 2, TRI_B_UPPER = 4 };
 
 // compute: DT_F64 (FP64 matrix cores), DT_F32 (FP32 matrix cores) or DT_F16 (FP16 matrix cores,
 // FP32 accumulation).  Either `d_tasks` (device array of ntasks tasks with identical M, N, K,

@@ -188,6 +188,10 @@ __global__ __launch_bounds__(NTHR) void k_gemm(const GemmTask* __restrict__ task
     }
     const GemmTask& T = tasks ? tasks[task] : one;
     const int m0 = (blk % bmc) * BM, n0 = (blk / bmc) * BN;
+    if ((T.tri & TRI_C_LOWER) && n0 >= m0 + BM) return;   // block strictly above the diagonal
+    int kend = T.K;                                       // products beyond kend are exact zeros
+    if (T.tri & TRI_A_LOWER) kend = min(kend, m0 + BM);
+    if (T.tri & TRI_B_UPPER) kend = min(kend, n0 + BN);
     const int t = threadIdx.x, l = t % 64, w = t / 64;
     const int wm = w / 2, wn = w % 2;
     const bool a_contig_r = T.transA == 0;   // A(m, k) at A[m + k*lda]
@@ -201,16 +205,16 @@ __global__ __launch_bounds__(NTHR) void k_gemm(const GemmTask* __restrict__ task
         for (int j = 0; j < 4; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
     SlabLoader<CT, EDGE> la, lb;
-    const int nk = (T.K + BK - 1) / BK;
-    la.load(T.A, T.ta, T.lda, a_contig_r, m0, 0, T.M, T.K, t);
-    lb.load(T.B, T.tb, T.ldb, b_contig_r, n0, 0, T.N, T.K, t);
+    const int nk = (kend + BK - 1) / BK;
+    la.load(T.A, T.ta, T.lda, a_contig_r, m0, 0, T.M, kend, t);
+    lb.load(T.B, T.tb, T.ldb, b_contig_r, n0, 0, T.N, kend, t);
     for (int kb = 0; kb < nk; ++kb) {
         la.store(As, a_contig_r, t);
         lb.store(Bs, b_contig_r, t);
         __syncthreads();
         if (kb + 1 < nk) {
-            la.load(T.A, T.ta, T.lda, a_contig_r, m0, (kb + 1) * BK, T.M, T.K, t);
-            lb.load(T.B, T.tb, T.ldb, b_contig_r, n0, (kb + 1) * BK, T.N, T.K, t);
+            la.load(T.A, T.ta, T.lda, a_contig_r, m0, (kb + 1) * BK, T.M, kend, t);
+            lb.load(T.B, T.tb, T.ldb, b_contig_r, n0, (kb + 1) * BK, T.N, kend, t);
         }
         if constexpr (sizeof(CT) == 2) {
             h8 af[4], bf[4];
@@ -435,6 +439,10 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     gptr<TB> Bp = (gptr<TB>)T.B;
     gptr_mut<TC> Cp = (gptr_mut<TC>)T.C;
     const int m0 = (blk % bmc) * TBM, n0 = (blk / bmc) * TBN;
+    if ((T.tri & TRI_C_LOWER) && n0 >= m0 + TBM) return;   // block strictly above the diagonal
+    int kend = T.K;                                        // products beyond kend are exact zeros
+    if (T.tri & TRI_A_LOWER) kend = min(kend, m0 + TBM);
+    if (T.tri & TRI_B_UPPER) kend = min(kend, n0 + TBN);
     const int t = threadIdx.x, l = t % 64, w = t / 64;
     const int wm = w % WMW, wn = w / WMW;
     typedef typename AccT<CT>::type Acc;
@@ -455,17 +463,17 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
 
     SA la;
     SB lb;
-    const int nk = (T.K + BK - 1) / BK;
+    const int nk = (kend + BK - 1) / BK;
     // Operand slabs are prefetched two ahead: slab 0 goes to LDS and slab 1 stays in registers;
     // during slab kb each register vector is stored into the other LDS buffer (slab kb + 1) and
     // then reloaded from global memory with slab kb + 2, spread over the slab's steps.
-    la.load(Ap, T.lda, m0, 0, T.M, T.K, t);
-    lb.load(Bp, T.ldb, n0, 0, T.N, T.K, t);
+    la.load(Ap, T.lda, m0, 0, T.M, kend, t);
+    lb.load(Bp, T.ldb, n0, 0, T.N, kend, t);
     la.store(As[0], t);
     lb.store(Bs[0], t);
     if (nk > 1) {
-        la.load(Ap, T.lda, m0, BK, T.M, T.K, t);
-        lb.load(Bp, T.ldb, n0, BK, T.N, T.K, t);
+        la.load(Ap, T.lda, m0, BK, T.M, kend, t);
+        lb.load(Bp, T.ldb, n0, BK, T.N, kend, t);
     }
     __syncthreads();
 
@@ -524,10 +532,10 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
                     if (vq * (NST - 1) / NV != st) continue;
                     if (vq < SA::VPT) {
                         la.store_q(vq, As[cur ^ 1], t);
-                        if constexpr (LD) la.load_q(vq, Ap, T.lda, m0, (kb + 2) * BK, T.M, T.K, t);
+                        if constexpr (LD) la.load_q(vq, Ap, T.lda, m0, (kb + 2) * BK, T.M, kend, t);
                     } else {
                         lb.store_q(vq - SA::VPT, Bs[cur ^ 1], t);
-                        if constexpr (LD) lb.load_q(vq - SA::VPT, Bp, T.ldb, n0, (kb + 2) * BK, T.N, T.K, t);
+                        if constexpr (LD) lb.load_q(vq - SA::VPT, Bp, T.ldb, n0, (kb + 2) * BK, T.N, kend, t);
                     }
                 }
                 if (st + 1 == NST) {

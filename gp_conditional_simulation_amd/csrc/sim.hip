@@ -312,6 +312,7 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
             g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
             g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
             g.alpha = 1.0; g.beta = 0.0;
+            g.tri = TRI_A_LOWER;   // L_kk is lower triangular
             dg.push_back(g);
         }
         // off-diagonal part of tile row i: one FP16 product of the row panel (nb x i nb) with
@@ -348,6 +349,7 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
             g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
             g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
             g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
+            g.tri = TRI_A_LOWER;   // L_kk is lower triangular
             r = gemm_launch(ctx, s, amp ? DT_F32 : DT_F64, nullptr, 1, g, GEMM_TRMM);
             for (int64_t gi = gbeg[(size_t)k]; r >= 0 && gi < gbeg[(size_t)k + 1]; ++gi) {
                 const Group& G = groups[(size_t)gi];
