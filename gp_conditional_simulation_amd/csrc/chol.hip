@@ -4,7 +4,7 @@
 // Sec. IV-B and Algorithm 2 (step 12): the scaled covariance s^2 V, cut into nb x nb tiles with a
 // per-tile precision map, is factored right-looking.  Step k:
 //   * diagonal tile (k, k): FP64 POTRF.  Here it is factored together with its explicit inverse
-//     T_k = L_kk^-1 by recursive halving down to a single-workgroup 64 x 64 leaf (LDS resident);
+//     T_k = L_kk^-1 by recursive halving down to a single-wavefront 64 x 64 leaf (register resident);
 //     the halves are joined with FP64 matrix-core GEMMs.
 //   * panel tiles (i, k), i > k: L_ik = A_ik L_kk^-T evaluated as the product A_ik T_k^T on FP64
 //     matrix cores for every tile and rounded once to the tile's storage precision (one batched
@@ -80,70 +80,81 @@ __global__ void k_copy_tasks(const CopyTask* tasks, int64_t chunk) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Leaf: factor an n x n (n <= 64) FP64 block in LDS and invert its factor.
-//   Cholesky: right-looking over columns, three barriers per column.
-//   Inverse: thread j computes column j of L^-1 by forward substitution.
-// Writes L (upper part zeroed) back to A and L^-1 (upper zeroed) to T.  A non-positive pivot at
-// local column k records col0 + k + 1 in flags[FLAG_INFO] unless an earlier failure is recorded.
+// Leaf: factor an n x n (n <= 64) FP64 block and invert its factor in one wavefront, without
+// barriers.  Lane i holds row i in registers (rows n..63 are identity padding).
+//   Cholesky, right-looking: at column k the pivot is read from lane k, lane i scales its entry to
+//   l_ik, and every lane updates its row with l_ik l_jk, l_jk read from lane j.
+//   Inverse, forward substitution L X = I by rows: x_i accumulates sum_{q<i} l_iq X_q; row p of
+//   X = (e_p - x_p) / l_pp is final once the rows above it have been applied, and is read from
+//   lane p and applied to the rows below it.
+// Writes L (upper part zeroed) back to A and L^-1 (upper part zeroed) to T.  A non-positive pivot
+// at local column k records col0 + k + 1 in flags[FLAG_INFO] unless an earlier failure is recorded.
 constexpr int LEAF = 64;
 
-__global__ __launch_bounds__(256) void k_potrf_leaf(double* A, int64_t lda, double* T, int64_t ldt,
-                                                    int n, int64_t col0, unsigned long long* flags) {
-    __shared__ double s[LEAF][LEAF + 1];
-    __shared__ double x[LEAF][LEAF + 1];
-    const int tid = threadIdx.x;
-    for (int idx = tid; idx < n * n; idx += 256) {
-        int i = idx % n, j = idx / n;
-        s[i][j] = (i >= j) ? A[i + (int64_t)j * lda] : 0.0;
-    }
-    __syncthreads();
+__device__ __forceinline__ double lane_read(double v, int lane) {
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
+    return __hiloint2double(hi, lo);
+}
+
+__global__ __launch_bounds__(LEAF) void k_potrf_leaf(double* A, int64_t lda, double* T, int64_t ldt,
+                                                     int n, int64_t col0, unsigned long long* flags) {
+    __shared__ double Ls[LEAF][LEAF + 1];
+    const int i = threadIdx.x;
+    double a[LEAF];
+#pragma unroll
+    for (int j = 0; j < LEAF; ++j) a[j] = (j <= i && i < n) ? A[i + (int64_t)j * lda] : (i == j ? 1.0 : 0.0);
+    double dii = 1.0;
     int bad = 0;
-    for (int k = 0; k < n; ++k) {
-        double akk = s[k][k];
+#pragma unroll
+    for (int k = 0; k < LEAF; ++k) {
+        const double akk = lane_read(a[k], k);
         if (!(akk > 0.0)) {
             bad = k + 1;
             break;
         }
-        double lkk = sqrt(akk);
-        __syncthreads();
-        for (int i = k + tid; i < n; i += 256) s[i][k] = (i == k) ? lkk : s[i][k] / lkk;
-        __syncthreads();
-        int m = n - k - 1;
-        for (int idx = tid; idx < m * m; idx += 256) {
-            int ii = k + 1 + idx % m, jj = k + 1 + idx / m;
-            if (ii >= jj) s[ii][jj] -= s[ii][k] * s[jj][k];
-        }
-        __syncthreads();
+        const double lkk = sqrt(akk);
+        const double lik = (i > k) ? a[k] / lkk : (i == k ? lkk : 0.0);
+        if (i == k) dii = lkk;
+        a[k] = lik;
+#pragma unroll
+        for (int j = k + 1; j < LEAF; ++j) a[j] -= lik * lane_read(lik, j);
     }
     if (bad) {
-        if (tid == 0 && flags)
-            atomicCAS(&flags[FLAG_INFO], 0ull, (unsigned long long)(col0 + bad));
+        if (i == 0 && flags) atomicCAS(&flags[FLAG_INFO], 0ull, (unsigned long long)(col0 + bad));
         return;
     }
-    // inverse of the lower-triangular factor, column by column
-    if (tid < n) {
-        int j = tid;
-        for (int i = 0; i < j; ++i) x[i][j] = 0.0;
-        x[j][j] = 1.0 / s[j][j];
-        for (int i = j + 1; i < n; ++i) {
-            double acc = 0.0;
-            for (int p = j; p < i; ++p) acc += s[i][p] * x[p][j];
-            x[i][j] = -acc / s[i][i];
+#pragma unroll
+    for (int j = 0; j < LEAF; ++j) {
+        const double v = (j <= i) ? a[j] : 0.0;
+        Ls[i][j] = v;
+        if (i < n && j < n) A[i + (int64_t)j * lda] = v;
+    }
+    // Ls row i is only read back by lane i itself: no barrier is needed
+    const double rii = 1.0 / dii;
+    double x[LEAF];
+#pragma unroll
+    for (int j = 0; j < LEAF; ++j) x[j] = 0.0;
+#pragma unroll
+    for (int p = 0; p < LEAF - 1; ++p) {
+        const double rpp = lane_read(rii, p);
+        const double lip = (i > p) ? Ls[i][p] : 0.0;   // rows at or above p receive exact zeros
+#pragma unroll
+        for (int j = 0; j <= p; ++j) {
+            const double xpj = ((p == j ? 1.0 : 0.0) - lane_read(x[j], p)) * rpp;   // X[p][j]
+            x[j] += lip * xpj;
         }
     }
-    __syncthreads();
-    for (int idx = tid; idx < n * n; idx += 256) {
-        int i = idx % n, j = idx / n;
-        A[i + (int64_t)j * lda] = (i >= j) ? s[i][j] : 0.0;
-        T[i + (int64_t)j * ldt] = x[i][j];
-    }
+#pragma unroll
+    for (int j = 0; j < LEAF; ++j)
+        if (i < n && j < n) T[i + (int64_t)j * ldt] = (j <= i) ? ((i == j ? 1.0 : 0.0) - x[j]) * rii : 0.0;
 }
 
 int potrf_inv(gpex_ctx_t ctx, hipStream_t s, double* A, int64_t lda, double* T, int64_t ldt, int n,
               double* ws, int64_t col0) {
     auto* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
     if (n <= LEAF) {
-        hipLaunchKernelGGL(k_potrf_leaf, dim3(1), dim3(256), 0, s, A, lda, T, ldt, n, col0, fl);
+        hipLaunchKernelGGL(k_potrf_leaf, dim3(1), dim3(LEAF), 0, s, A, lda, T, ldt, n, col0, fl);
         GPEX_HIP(ctx, hipGetLastError());
         return GPEX_OK;
     }

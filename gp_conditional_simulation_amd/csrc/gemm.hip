@@ -329,17 +329,47 @@ struct TSlab {
     static constexpr int LDK = BK + TCfg<CT>::PAD;               // [row][k] row stride
     static constexpr int LDR = ROWS + (sizeof(CT) == 8 ? 4 : 8); // [k][row] k stride
     static constexpr int ELEMS = KROW ? BK * LDR : ROWS * LDK;
-    // elements per vector: 16-byte loads for k-contiguous FP16 operands, else 4 elements
-    static constexpr int VE = (!CR && sizeof(T) == 2 && sizeof(CT) == 2) ? 8 : 4;
-    static constexpr int VPT = (ROWS * BK / THREADS) / VE;
+    // Micro-block path (FP16 compute, row index contiguous): each thread loads MR consecutive rows
+    // in each of KB consecutive k and writes them transposed, KB consecutive k per row, so that the
+    // [row][k] LDS layout the FP16 fragments need is filled with 2 KB-byte stores instead of
+    // 2-byte ones.  Consecutive lanes take consecutive k groups of one row block: their stores
+    // cover a row contiguously (no bank conflicts) and their loads 64-byte column segments.
+    static constexpr bool MB = CR && sizeof(CT) == 2;
+    static constexpr int MR = 8;
+    static constexpr int KB = MB ? ROWS * BK / (MR * THREADS) : 1;
+    static constexpr int KG = BK / KB;                            // k groups per slab (MB)
+    static_assert(!MB || (KB >= 2 && ROWS * BK == MR * KB * THREADS), "micro-blocks must tile the slab");
+    // elements per vector: 16-byte loads for k-contiguous FP16 operands, MR rows on the
+    // micro-block path, else 4 elements
+    static constexpr int VE = MB ? MR : (!CR && sizeof(T) == 2 && sizeof(CT) == 2) ? 8 : 4;
+    static constexpr int VPT = MB ? 1 : (ROWS * BK / THREADS) / VE;
     static constexpr int TPK = ROWS / VE;                         // threads per k-row (CR)
-    static_assert(VPT >= 1 && (ROWS * BK) % (THREADS * VE) == 0, "slab must split evenly over the threads");
-    CT v[VPT][VE];
+    static_assert(MB || (VPT >= 1 && (ROWS * BK) % (THREADS * VE) == 0), "slab must split evenly over the threads");
+    CT v[MB ? KB : VPT][VE];
 
     __device__ __forceinline__ static int idx(int row, int k) { return KROW ? k * LDR + row : row * LDK + k; }
 
     // Vector q of this thread's share of the slab at (r0, k0), from global memory into registers.
     __device__ __forceinline__ void load_q(int q, gptr<T> base, int64_t ld, int r0, int k0, int R, int K, int t) {
+        if constexpr (MB) {
+            const int r = (t / KG) * MR, k = (t % KG) * KB;
+            const int gr = r0 + r;
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                const int gk = k0 + k + kk;
+                if (!EDGE) {
+                    typedef typename VN<T, MR>::type VT;
+                    VT x = *reinterpret_cast<const __attribute__((address_space(1))) VT*>(base + (int64_t)gr + (int64_t)gk * ld);
+#pragma unroll
+                    for (int e = 0; e < MR; ++e) v[kk][e] = to_ct<CT, T>(x[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < MR; ++e)
+                        v[kk][e] = (gr + e < R && gk < K) ? to_ct<CT, T>(base[(int64_t)(gr + e) + (int64_t)gk * ld]) : CT(0);
+                }
+            }
+            return;
+        }
         int r, k;
         if (CR) {
             r = (t % TPK) * VE;
@@ -375,6 +405,18 @@ struct TSlab {
 
     // Vector q of the registers into the LDS slab.
     __device__ __forceinline__ void store_q(int q, CT* sm, int t) {
+        if constexpr (MB) {
+            const int r = (t / KG) * MR, k = (t % KG) * KB;
+            typedef typename VN<CT, KB>::type WT;
+#pragma unroll
+            for (int e = 0; e < MR; ++e) {
+                WT w;
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) w[kk] = v[kk][e];
+                *reinterpret_cast<WT*>(&sm[idx(r + e, k)]) = w;
+            }
+            return;
+        }
         if (CR) {
             int r = (t % TPK) * VE, k = t / TPK + (THREADS / TPK) * q;
 #pragma unroll
