@@ -110,8 +110,6 @@ enum : int { TRI_C_LOWER = 1, TRI_A_LOWER = 2, TRI_B_UPPER = 4 };
 // is skipped.
 enum : int { GEMM_GENERIC = 0, GEMM_UPDATE = 1, GEMM_TRMM = 2 };
 extern int g_f16_grid;   // wave grid of FP16 TRMM launches (-1 auto, 0: 2 x 2, 1: 4 x 2, 2: 2 x 4)
-extern int g_f64_waves4; // FP64 typed launches with eight 64 x 32 waves per 128 x 128 block (0 off, 1 on)
-extern int g_f64_wide;
 extern int g_gemm_interleave; // typed launches with products and memory instructions interleaved one by one (0 off, 1 on)   // FP64 typed launches with 64 x 128 waves (-1 auto, 0 off, 1 when the shape allows)
 int gemm_launch(gpex_ctx_t ctx, hipStream_t s, int compute, const GemmTask* d_tasks, int ntasks,
                 const GemmTask& one, int role = GEMM_GENERIC);

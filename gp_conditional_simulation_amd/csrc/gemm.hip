@@ -35,8 +35,6 @@ constexpr int BM = 128, BN = 128, NTHR = 256;
 // Wave grid of FP16 TRMM launches: -1 = chosen per launch (2 x 4 waves when that still gives at
 // least 2048 workgroups, else 2 x 2), 0 = 2 x 2 waves (128 x 128), 1 = 4 x 2, 2 = 2 x 4.
 int g_f16_grid = -1;
-int g_f64_wide = 0;
-int g_f64_waves4 = 0;
 int g_gemm_interleave = 1;
 
 template <typename CT> struct Cfg;
@@ -435,18 +433,11 @@ struct TSlab {
     }
 };
 
-// Waves resident per SIMD for a wave tile of 64 x (16 FJ).
-template <int FJ> struct WavesPerEU { static constexpr int v = FJ == 8 ? 1 : FJ == 2 ? 4 : 2; };
-
-// WMW x WNW waves of 64 x (16 FJ) each: a block of (64 WMW) x (16 FJ WNW) outputs per workgroup.
-// FJ = 4: 64 x 64 per wave, two waves per SIMD.  FJ = 2: 64 x 32 per wave, four waves per SIMD
-// (a single wave issues FP64 matrix-core ops at only about half the pipe's rate, so the more
-// waves are ready to issue, the less a stalled one costs).  FJ = 8: 64 x 128 per wave, its 128
-// FP64 accumulators filling the accumulation registers, one wave per SIMD.
+// WMW x WNW waves of 64 x (16 FJ) each: a block of (64 WMW) x (16 FJ WNW) outputs per workgroup,
+// two waves per SIMD (accumulators in vector registers: with FJ = 4 they take 128 of them).
 template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, bool EDGE, int ROLE,
           int WMW = 2, int WNW = 2, int FJ = 4, int INTERLEAVE = 0>
-__global__ __launch_bounds__(64 * WMW * WNW)
-__attribute__((amdgpu_waves_per_eu(WavesPerEU<FJ>::v, WavesPerEU<FJ>::v)))
+__global__ __launch_bounds__(64 * WMW * WNW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int bmc, int bnc, int xcd_map,
               unsigned long long* flags) {
     constexpr int BK = TCfg<CT>::BK;
@@ -488,20 +479,11 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     const int t = threadIdx.x, l = t % 64, w = t / 64;
     const int wm = w % WMW, wn = w / WMW;
     typedef typename AccT<CT>::type Acc;
-    // With FJ = 8 the accumulators live in the accumulation registers; zeroing them with a
-    // matrix-core op (rather than vector moves) keeps the loop-carried values in that register
-    // class, where the compiler otherwise shuttles them through the vector registers every slab.
     Acc acc[4][FJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < FJ; ++j) {
-            acc[i][j] = Acc{0, 0, 0, 0};
-            if constexpr (FJ == 8) {
-                if constexpr (sizeof(CT) == 2) mma(acc[i][j], h8{}, h8{});
-                else mma(acc[i][j], (CT)0, (CT)0);
-            }
-        }
+        for (int j = 0; j < FJ; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
     SA la;
     SB lb;
@@ -698,24 +680,6 @@ static int try_typed(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
             else
                 hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4>), dim3((unsigned)grid2),
                                    dim3(512), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
-            return 1;
-        }
-    }
-    if constexpr (sizeof(CT) == 8) {
-        if (fast && g_f64_waves4) {
-            // 128 x 128 blocks of eight 64 x 32 waves, two blocks per CU: four waves per SIMD
-            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4, 2>), dim3((unsigned)grid),
-                               dim3(512), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
-            return 1;
-        }
-        // 128 x 256 blocks of four 64 x 128 waves when the launch still fills the chip twice over
-        int wide = g_f64_wide;
-        if (wide < 0) wide = (int64_t)ntasks * (one.M / 128) * (one.N / 256) >= 512;
-        if (fast && wide && one.M % 128 == 0 && one.N % 256 == 0) {
-            const int bmc2 = one.M / 128, bnc2 = one.N / 256, bpt2 = bmc2 * bnc2;
-            int64_t grid2 = xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt2 : (int64_t)ntasks * bpt2;
-            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 2, 8>), dim3((unsigned)grid2),
-                               dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
             return 1;
         }
     }
