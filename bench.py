@@ -14,7 +14,7 @@ Phase times come from HIP events on the library's stream; the dominant kernel's 
 the library's own per-launch events.  The CPU baseline times the oracle on a bounded leading
 block of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--trmm-sweep]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--trmm-sweep | --krige]
 """
 import argparse
 import json
@@ -162,6 +162,77 @@ def trmm_sweep(args):
                       "fp64_peak_tflops": PEAK_TF["fp64"], "max_x_fp64_peak": best, "points": rows}), flush=True)
 
 
+def krige_bench(args):
+    """The kriging workload's conditional path, one step: universal kriging (W, z_hat, v), joint
+    covariance tiles + factor, seeded simulations, conditioning + scan + calibration of the regions
+    (20,000 prediction + 20,000 observation locations, Matern nu = 3/2, range 0.1, trend
+    (0.5, 1, -1), tau^2 = 0.01, FP64, 1,000 simulations, u = 1, level 0.9).  The observations are
+    the trend plus seeded N(0, 1) noise: the work does not depend on their values.  Reported as
+    nsim / (T_trmm + T_cond+scan) with the factor amortised, and per phase."""
+    import numpy as np
+    import torch
+
+    import gp_conditional_simulation_amd as g
+    import gpex_synth as syn
+
+    w = syn.workload("krige20k")
+    x, y = w.locations()
+    n_p, n_o = w.n_pred, w.n_obs
+    dev = torch.device("cuda:0")
+    f64 = lambda a: torch.tensor(np.ascontiguousarray(a), dtype=torch.float64, device=dev)   # noqa: E731
+    xp, yp, xo, yo = x[:n_p], y[:n_p], x[n_p:], y[n_p:]
+    y_o = syn.trend_mean(xo, yo, w.trend) + np.random.default_rng(w.seed_sim).standard_normal(n_o)
+    params = {"kind": w.kind, "sigma2": w.sigma2, "range": w.beta, "nu": w.nu}
+    diag_add = f64(np.r_[np.zeros(n_p), np.full(n_o, w.tau2)])
+    loc, loc_o, loc_p, dy = f64(np.r_[x, y]), f64(np.r_[xo, yo]), f64(np.r_[xp, yp]), f64(y_o)
+    ctx = g.Context(0)
+    M = g.colmajor(w.n, w.nsim, ctx)
+    torch.cuda.synchronize()
+
+    def step():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record()
+        W, zhat, v, info = g.krige(ctx, loc_o, n_o, loc_p, n_p, dy, 3, params, w.tau2, w.nb)
+        ev[1].record()
+        A = g.cov_gen(ctx, loc, w.n, dict(params, nugget=0.0), w.nb, amp=w.amp, tol=w.tol, diag_add=diag_add)
+        ev[2].record()
+        fi = g.potrf_mp(ctx, A)
+        ev[3].record()
+        g.trmm_sim(ctx, A, w.nsim, seed=w.seed_sim, M=M, want_diag=False)
+        ev[4].record()
+        out = g.excursion_regions(ctx, M, n_p, n_o, w.nsim, w.u, w.level, W=W, y_o=dy, zhat=zhat, v=v)
+        ev[5].record()
+        torch.cuda.synchronize()
+        A.close()
+        if info != 0 or fi != 0 or out["status"] != 0:
+            raise RuntimeError(f"kriging workload failed: krige {info}, potrf {fi}, regions {out['status']}")
+        ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
+        return dict(zip(("krige", "cov_gen", "potrf", "trmm", "cond_scan_regions"), ms),
+                    cin=int(out["cin"].sum().item()), cout=int(out["cout"].sum().item()))
+
+    for i in range(args.warmup):
+        log("warmup", i, step())
+    recs = []
+    for i in range(args.steps):
+        r = step()
+        recs.append(r)
+        log("step", i, {k: round(v, 2) for k, v in r.items()})
+    med = {k: statistics.median(r[k] for r in recs) for k in ("krige", "cov_gen", "potrf", "trmm", "cond_scan_regions")}
+    cond_flops = 2.0 * n_p * w.nsim * n_o
+    krige_flops = n_o ** 3 / 3.0 + 2.0 * n_o ** 2 * n_p
+    print(json.dumps({
+        "metric": "conditional simulations / s, kriging workload (nsim / (T_trmm + T_cond+scan))",
+        "value": round(w.nsim / ((med["trmm"] + med["cond_scan_regions"]) * 1e-3), 1), "unit": "simulations/s",
+        "config": {"workload": "krige20k: 20,000 prediction + 20,000 observation locations, Matern nu=1.5 range=0.1, "
+                               "trend (0.5, 1, -1), tau2 0.01, FP64 tiles, tile 512, nsim 1000, u 1, level 0.9"},
+        "steps": args.steps, "warmup": args.warmup, "phase_ms_median": {k: round(v, 2) for k, v in med.items()},
+        "krige_fp64_tflops": round(krige_flops / (med["krige"] * 1e-3) / 1e12, 1),
+        "joint_potrf_fp64_tflops": round(w.n ** 3 / 3.0 / (med["potrf"] * 1e-3) / 1e12, 1),
+        "conditioning_fp64_tflops_lower_bound": round(cond_flops / (med["cond_scan_regions"] * 1e-3) / 1e12, 1),
+        "regions_cells": {"cin": recs[-1]["cin"], "cout": recs[-1]["cout"]},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +245,8 @@ def main():
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     ap.add_argument("--trmm-sweep", action="store_true",
                     help="TRMM throughput against N at three correlation levels instead of the step benchmark")
+    ap.add_argument("--krige", action="store_true",
+                    help="the kriging workload's conditional path instead of the step benchmark")
     ap.add_argument("--sweep-nsim", type=int, default=2048)
     ap.add_argument("--sweep-max-n", type=int, default=131072)
     args = ap.parse_args()
@@ -183,6 +256,9 @@ def main():
         sys.exit(2)
     if args.trmm_sweep:
         trmm_sweep(args)
+        return
+    if args.krige:
+        krige_bench(args)
         return
 
     import numpy as np

@@ -715,9 +715,12 @@ static int launch_ct(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
     // typed fast kernels for the operand-type combinations of the hot launches
     bool tfast = (M % BM == 0) && (N % BN == 0) && (K % TCfg<CT>::BK == 0) && (one.lda % 8 == 0) &&
                  (one.ldb % 8 == 0) && al(one.A) && al(one.B);
-    // NT form (trailing updates, panel solves) and NN form (TRMM) with uniform or TRMM/TRSM types
+    // NT form (trailing updates, panel solves), NN form (TRMM, blocked solves) and TN form with uniform
+    // types, and the TRMM/TRSM operand mixes
     int done = try_typed<CT, CT, CT, CT, 0, 1, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
     if (!done) done = try_typed<CT, CT, CT, CT, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
+    // TN form (conditioning product W^T R, transposed blocked solves)
+    if (!done) done = try_typed<CT, CT, CT, CT, 1, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
     if constexpr (sizeof(CT) == 2) {
         if (!done) done = try_typed<CT, _Float16, _Float16, double, 1, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);
         if (!done) done = try_typed<CT, double, _Float16, double, 0, 0, ROLE>(ctx, s, d_tasks, ntasks, one, tfast, grid, bmc, bnc, xcd, fl);

@@ -16,6 +16,8 @@
 #include <algorithm>
 #include <cmath>
 
+#include <vector>
+
 #include "common.h"
 
 namespace gpex {
@@ -97,28 +99,73 @@ static unsigned nblk(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 // In place B (n x m, leading dim ldb, n = L->n) <- L^-1 B (trans = 0) or L^-T B (trans = 1), using
 // the tiles of the FP64 factor and the inverse diagonal tiles.  tmp: nb x m FP64 scratch.
+// Step k applies T_k (or T_k^T) to block row k, then subtracts its contribution from every block
+// row still to be solved in one batched launch (the full-height rows; a ragged last row of tiles
+// gets a launch of its own).
 static int tile_trsm(gpex_ctx_t ctx, gpex_tiled_t L, double* B, int64_t ldb, int64_t m, int trans, double* tmp) {
     const int64_t nt = L->nt, nb = L->nb, n = L->n;
+    hipStream_t s = ctx->stream;
     auto rows = [&](int64_t k) { return std::min<int64_t>(nb, n - k * nb); };
+    struct Step { int64_t k, b0, b1; bool ragged; };
+    std::vector<GemmTask> tasks;
+    std::vector<Step> steps;
+    auto task = [&](int64_t i, int64_t k) {
+        GemmTask g{};
+        g.A = trans ? L->tile(k, i) : L->tile(i, k); g.ta = DT_F64; g.lda = nb; g.transA = (int8_t)trans;
+        g.B = B + k * nb; g.tb = DT_F64; g.ldb = ldb; g.transB = 0;
+        g.C = B + i * nb; g.tc = DT_F64; g.ldc = ldb;
+        g.M = (int)rows(i); g.N = (int)m; g.K = (int)rows(k);
+        g.alpha = -1.0; g.beta = 1.0;
+        return g;
+    };
     for (int64_t step = 0; step < nt; ++step) {
-        int64_t k = trans ? nt - 1 - step : step;
-        int64_t rk = rows(k);
-        double* Bk = B + k * nb;
-        // Bk <- T_k Bk  (or T_k^T Bk)
-        GPEX_TRY(gemm1(ctx, DT_F64, L->tinv_tile(k), DT_F64, trans, nb, Bk, DT_F64, 0, ldb, tmp, DT_F64, nb,
-                       (int)rk, (int)m, (int)rk, 1.0, 0.0));
-        GPEX_TRY(copy2d(ctx, ctx->stream, tmp, DT_F64, nb, Bk, DT_F64, ldb, rk, m, 1.0));
-        if (!trans) {
-            for (int64_t i = k + 1; i < nt; ++i)   // B_i -= L_ik B_k
-                GPEX_TRY(gemm1(ctx, DT_F64, L->tile(i, k), DT_F64, 0, nb, Bk, DT_F64, 0, ldb, B + i * nb,
-                               DT_F64, ldb, (int)rows(i), (int)m, (int)rk, -1.0, 1.0));
-        } else {
-            for (int64_t i = 0; i < k; ++i)        // B_i -= L_ki^T B_k
-                GPEX_TRY(gemm1(ctx, DT_F64, L->tile(k, i), DT_F64, 1, nb, Bk, DT_F64, 0, ldb, B + i * nb,
-                               DT_F64, ldb, (int)nb, (int)m, (int)rk, -1.0, 1.0));
+        const int64_t k = trans ? nt - 1 - step : step;
+        Step st{k, (int64_t)tasks.size(), 0, false};
+        if (!trans) {   // B_i -= L_ik B_k, i > k
+            for (int64_t i = k + 1; i < nt; ++i)
+                if (rows(i) == nb) tasks.push_back(task(i, k));
+            st.ragged = k + 1 < nt && rows(nt - 1) < nb;
+        } else {        // B_i -= L_ki^T B_k, i < k (all full height)
+            for (int64_t i = 0; i < k; ++i) tasks.push_back(task(i, k));
+        }
+        st.b1 = (int64_t)tasks.size();
+        steps.push_back(st);
+    }
+    GemmTask* d_tasks = nullptr;
+    if (!tasks.empty()) {
+        GPEX_TRY(dev_alloc(ctx, (void**)&d_tasks, sizeof(GemmTask) * tasks.size(), "solve tasks"));
+        if (hipMemcpy(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice) != hipSuccess) {
+            dev_free(d_tasks);
+            return set_err(ctx, GPEX_ERR_HIP, "solve task upload");
         }
     }
-    return GPEX_OK;
+    int r = GPEX_OK;
+    for (const Step& st : steps) {
+        const int64_t k = st.k, rk = rows(k);
+        double* Bk = B + k * nb;
+        // Bk <- T_k Bk  (or T_k^T Bk); T_k is lower triangular
+        GemmTask d{};
+        d.A = L->tinv_tile(k); d.ta = DT_F64; d.lda = nb; d.transA = (int8_t)trans;
+        d.B = Bk; d.tb = DT_F64; d.ldb = ldb; d.transB = 0;
+        d.C = tmp; d.tc = DT_F64; d.ldc = nb;
+        d.M = (int)rk; d.N = (int)m; d.K = (int)rk; d.alpha = 1.0; d.beta = 0.0;
+        d.tri = trans ? 0 : TRI_A_LOWER;
+        r = gemm_launch(ctx, s, DT_F64, nullptr, 1, d);
+        if (r >= 0) r = copy2d(ctx, s, tmp, DT_F64, nb, Bk, DT_F64, ldb, rk, m, 1.0);
+        if (r >= 0 && st.b1 > st.b0)
+            r = gemm_launch(ctx, s, DT_F64, d_tasks + st.b0, (int)(st.b1 - st.b0), tasks[(size_t)st.b0]);
+        if (r >= 0 && st.ragged) {
+            GemmTask g = task(nt - 1, k);
+            r = gemm_launch(ctx, s, DT_F64, nullptr, 1, g);
+        }
+        if (r < 0) break;
+    }
+    // the task list is released once the queued launches no longer read it
+    if (d_tasks) {
+        if (hipStreamSynchronize(s) != hipSuccess && r >= 0) r = set_err(ctx, GPEX_ERR_HIP, "solve sync");
+        dev_free(d_tasks);
+    }
+    return r;
 }
 
 }  // namespace gpex
