@@ -259,13 +259,23 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     int r = dev_alloc(ctx, &B, (size_t)rows * cols * (amp ? 2 : 8), "simulation input B");
     if (r >= 0) r = dev_alloc(ctx, (void**)&Mp, sizeof(double) * rows * cols, "padded M");
     if (r >= 0) r = dev_alloc(ctx, (void**)&part, sizeof(double) * nblkB, "norm partials");
-    // off-diagonal tasks for every step, built once and grouped by the factor tile's storage type
-    // (one typed kernel per launch)
+    // An all-FP64 factor whose tiles of each row are stored back to back (column-major nb x nb
+    // tiles with no alignment gap): the off-diagonal tiles of row i then form one column-major
+    // nb x (i nb) matrix with leading dimension nb, so the row's whole contribution is one product.
+    bool rowpanel64 = !amp && nt > 1;
+    for (int64_t i = 1; rowpanel64 && i < nt; ++i)
+        for (int64_t j = 0; rowpanel64 && j < i; ++j)
+            rowpanel64 = L->prec(i, j) == DT_F64 &&
+                         (j == 0 || static_cast<uint8_t*>(L->tile(i, j)) ==
+                                        static_cast<uint8_t*>(L->tile(i, j - 1)) + (size_t)nb * nb * 8);
+    const bool fused = (amp && L->l16) || rowpanel64;
+    // otherwise: off-diagonal tasks for every step, built once and grouped by the factor tile's
+    // storage type (one typed kernel per launch)
     struct Group { int64_t b0, b1; };
     std::vector<GemmTask> tasks;
     std::vector<Group> groups;
     std::vector<int64_t> gbeg((size_t)nt + 1, 0);
-    for (int64_t k = 0; k < nt; ++k) {
+    for (int64_t k = 0; k < nt && !fused; ++k) {
         gbeg[(size_t)k] = (int64_t)groups.size();
         for (int ta = DT_F64; ta <= DT_F16; ++ta) {
             int64_t b0 = (int64_t)tasks.size();
@@ -302,26 +312,32 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
                        1.0 / L->s, amp, B, part);
     if (hipGetLastError() != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "make_B launch"); }
     if (ctx->timing) (void)hipEventRecord(ev[1], s);
-    if (amp && L->l16) {
-        // diagonal tiles: FP32 products of cast32(L_kk) and cast32(B_k), one launch
+    if (fused) {
+        // diagonal tiles, one launch: FP32 products of cast32(L_kk) and cast32(B_k) (mixed
+        // precision) or FP64 products
         std::vector<GemmTask> dg;
         for (int64_t k = 0; k < nt; ++k) {
             GemmTask g{};
             g.A = L->tile(k, k); g.ta = DT_F64; g.lda = nb; g.transA = 0;
-            g.B = static_cast<_Float16*>(B) + (size_t)k * nb; g.tb = DT_F16; g.ldb = rows; g.transB = 0;
+            g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
+            g.ldb = rows; g.transB = 0;
             g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
             g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
             g.alpha = 1.0; g.beta = 0.0;
             g.tri = TRI_A_LOWER;   // L_kk is lower triangular
             dg.push_back(g);
         }
-        // off-diagonal part of tile row i: one FP16 product of the row panel (nb x i nb) with
-        // B[0 : i nb], longest rows first
+        // off-diagonal part of tile row i: one product of the row panel (nb x i nb) with
+        // B[0 : i nb], longest rows first: FP16 (the row-major cast16 panels) or FP64 (the tiles)
         std::vector<GemmTask> od;
         for (int64_t i = nt - 1; i >= 1; --i) {
             GemmTask g{};
-            g.A = L->l16_panel(i); g.ta = DT_F16; g.lda = i * nb; g.transA = 1;
-            g.B = B; g.tb = DT_F16; g.ldb = rows; g.transB = 0;
+            if (amp) {
+                g.A = L->l16_panel(i); g.ta = DT_F16; g.lda = i * nb; g.transA = 1;
+            } else {
+                g.A = L->tile(i, 0); g.ta = DT_F64; g.lda = nb; g.transA = 0;
+            }
+            g.B = B; g.tb = amp ? DT_F16 : DT_F64; g.ldb = rows; g.transB = 0;
             g.C = Mp + i * nb; g.tc = DT_F64; g.ldc = rows;
             g.M = (int)nb; g.N = (int)cols; g.K = (int)(i * nb);
             g.alpha = 1.0; g.beta = 1.0;
@@ -334,8 +350,9 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         if (r >= 0 && !od.empty() &&
             hipMemcpy(d2 + dg.size(), od.data(), sizeof(GemmTask) * od.size(), hipMemcpyHostToDevice) != hipSuccess)
             r = set_err(ctx, GPEX_ERR_HIP, "trmm task upload");
-        if (r >= 0) r = gemm_launch(ctx, s, DT_F32, d2, (int)dg.size(), dg[0], GEMM_TRMM);
-        if (r >= 0 && !od.empty()) r = gemm_launch(ctx, s, DT_F16, d2 + dg.size(), (int)od.size(), od[0], GEMM_TRMM);
+        if (r >= 0) r = gemm_launch(ctx, s, amp ? DT_F32 : DT_F64, d2, (int)dg.size(), dg[0], GEMM_TRMM);
+        if (r >= 0 && !od.empty())
+            r = gemm_launch(ctx, s, amp ? DT_F16 : DT_F64, d2 + dg.size(), (int)od.size(), od[0], GEMM_TRMM);
         // d2 is released after the stream synchronisation below
         dev_free(d_tasks);
         d_tasks = d2;
