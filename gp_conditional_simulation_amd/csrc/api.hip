@@ -61,6 +61,7 @@ extern "C" int gpex_ctx_destroy(gpex_ctx_t ctx) {
     if (ctx->stream) (void)hipStreamSynchronize(ctx->stream);
     else (void)hipDeviceSynchronize();
     dev_free(ctx->d_flags);
+    dev_free(ctx->sim_ws);
     delete ctx;
     return GPEX_OK;
 }

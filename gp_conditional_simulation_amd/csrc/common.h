@@ -26,6 +26,10 @@ struct gpex_ctx_s {
     long long* d_flags = nullptr;     // FLAG_COUNT device words
     bool timing = false;
     double timings[16] = {};          // layout documented at gpex_ctx_timings
+    // simulation workspace (FP16/FP64 input B, padded M, norm partials), kept between calls and
+    // grown when a call needs more
+    void* sim_ws = nullptr;
+    size_t sim_ws_bytes = 0;
 };
 
 struct gpex_tiled_s {

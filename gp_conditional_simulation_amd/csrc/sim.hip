@@ -254,11 +254,24 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     double* Mp = nullptr;
     double* part = nullptr;
     GemmTask* d_tasks = nullptr;
-    auto cleanup = [&]() { dev_free(B); dev_free(Mp); dev_free(part); dev_free(d_tasks); };
+    auto cleanup = [&]() { dev_free(d_tasks); };
     const int64_t nblkB = (rows * cols + 255) / 256;
-    int r = dev_alloc(ctx, &B, (size_t)rows * cols * (amp ? 2 : 8), "simulation input B");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&Mp, sizeof(double) * rows * cols, "padded M");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&part, sizeof(double) * nblkB, "norm partials");
+    auto al256 = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t bB = al256((size_t)rows * cols * (amp ? 2 : 8)), bM = al256(sizeof(double) * rows * cols),
+                 bP = al256(sizeof(double) * nblkB);
+    int r = GPEX_OK;
+    if (ctx->sim_ws_bytes < bB + bM + bP) {   // the previous call has completed: it synchronised
+        dev_free(ctx->sim_ws);
+        ctx->sim_ws = nullptr;
+        ctx->sim_ws_bytes = 0;
+        r = dev_alloc(ctx, &ctx->sim_ws, bB + bM + bP, "simulation workspace");
+        if (r >= 0) ctx->sim_ws_bytes = bB + bM + bP;
+    }
+    if (r >= 0) {
+        B = ctx->sim_ws;
+        Mp = reinterpret_cast<double*>(static_cast<uint8_t*>(ctx->sim_ws) + bB);
+        part = reinterpret_cast<double*>(static_cast<uint8_t*>(ctx->sim_ws) + bB + bM);
+    }
     // An all-FP64 factor whose tiles of each row are stored back to back (column-major nb x nb
     // tiles with no alignment gap): the off-diagonal tiles of row i then form one column-major
     // nb x (i nb) matrix with leading dimension nb, so the row's whole contribution is one product.

@@ -177,7 +177,9 @@ int gpex_normals(gpex_ctx_t ctx, uint64_t seed, uint32_t stream, int64_t n, int6
  * is converted to FP16 and multiplied on FP16 matrix cores, the diagonal tile is applied in
  * FP32, all with FP32 accumulation, and M is written in FP64; with amp = 0 everything is FP64.
  * d_M: n x nsim, leading dimension ldm >= n.  diag (may be NULL) receives norm_B.
- * Requires a factored matrix (GPEX_ERR_STATE otherwise).  Synchronises when diag != NULL. */
+ * Requires a factored matrix (GPEX_ERR_STATE otherwise).  Synchronises before returning.
+ * The context keeps the workspace of its largest call (the FP16 or FP64 input B and a padded
+ * copy of M: about (2 or 8) + 8 bytes per element of the padded n x nsim) until it is destroyed. */
 int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t l, int64_t nsim, uint64_t seed, const double* d_Z,
                   double* d_M, int64_t ldm, gpex_diag* diag);
 
