@@ -333,3 +333,69 @@ def test_regions_error_paths(ctx):
     v2 = dev(np.r_[np.ones(n_p - 1), 0.0])
     out = g.excursion_regions(ctx, M, n_p, 0, nsim, -5.0, 0.9, zhat=zhat, v=v2)
     assert out["status"] == g.ERR_MSPE_NONPOS
+
+
+# ---- edge cases: a single padded tile, n = 1, one and ragged simulation columns, kriging with
+# ---- fewer observations than a tile and a single prediction location
+
+@pytest.mark.parametrize("n,nb,nsim", [(1, 16, 1), (37, 64, 1), (100, 128, 129), (160, 160, 3), (161, 160, 257)],
+                         ids=lambda v: str(v))
+def test_small_and_ragged_fp64(ctx, n, nb, nsim):
+    x, y, params = setup_case(n, nb, 1.5, 0.2, 7)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=0)
+    assert g.potrf_mp(ctx, A) == 0
+    V = oracle.cov_matrix(x, y, 0, 1.0, 0.2, 1.5, nugget=1e-4)
+    Lo, info = oracle.potrf(V)
+    assert info == 0
+    Ld = A.to_dense().cpu().numpy()
+    assert rel(np.tril(Ld), Lo) <= 1e-12
+    assert np.all(np.triu(Ld, 1) == 0.0)
+    Z = syn.explicit_normals(n, nsim, 2001)
+    M, _ = g.trmm_sim(ctx, A, nsim, Z=dev_cm(Z))
+    Mo = oracle.trmm(Lo, Z)
+    assert rel(M.cpu().numpy(), Mo) <= 1e-12
+    out = g.excursion_regions(ctx, M, n, 0, nsim, 0.0)
+    so = oracle.scan(Mo, 0.0)
+    assert np.array_equal(out["counts"].cpu().numpy(), so["counts"])
+    assert np.array_equal(out["sizes"].cpu().numpy(), so["sizes"])
+    A.close()
+
+
+def test_single_tile_mixed_precision_simulation(ctx):
+    """One tile (no off-diagonal work): the mixed-precision product is the FP32 diagonal alone,
+    applied to B = Z / s rounded to FP16, with the scale s of Eq. 12 (no reduced-precision tile:
+    s = 65503).  This is the per-step product path (there are no row panels)."""
+    n, nb, nsim = 150, 160, 64
+    x, y, params = setup_case(n, nb, 0.5, 0.1, 9)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=1e-8)
+    assert g.potrf_mp(ctx, A) == 0
+    assert A.diag["tiles"] == [1, 0, 0]
+    Z = syn.explicit_normals(n, nsim, 2002)
+    M, d = g.trmm_sim(ctx, A, nsim, Z=dev_cm(Z))
+    Lo, _ = oracle.potrf(oracle.cov_matrix(x, y, 0, 1.0, 0.1, 0.5, nugget=1e-4))
+    Mo = oracle.trmm(Lo, Z)
+    assert rel(M.cpu().numpy(), Mo) <= 1e-2
+    s = A.diag["s"]
+    assert s == 65503.0
+    assert d["norm_B"] == pytest.approx(np.linalg.norm(Z / s), rel=1e-12)   # of Z / s before rounding
+    A.close()
+
+
+@pytest.mark.parametrize("n_o,n_p,nb", [(40, 1, 64), (3, 5, 16), (200, 1, 160)], ids=lambda v: str(v))
+def test_krige_small(ctx, n_o, n_p, nb):
+    xo, yo, xp, yp, y_obs = _krige_case(n_o, n_p, 31)
+    params = {"kind": 0, "sigma2": 1.0, "range": 0.1, "nu": 1.5}
+    W, zhat, v, info = g.krige(ctx, dev(np.r_[xo, yo]), n_o, dev(np.r_[xp, yp]), n_p, dev(y_obs), 3, params,
+                               0.01, nb)
+    assert info == 0
+    r = oracle.krige(xo, yo, xp, yp, y_obs, 3, 0, 1.0, 0.1, 1.5, 0.01)
+    assert rel(W.cpu().numpy(), r["W"]) <= 1e-9
+    assert rel(zhat.cpu().numpy(), r["zhat"]) <= 1e-9
+    assert rel(v.cpu().numpy(), r["v"]) <= 1e-9
+
+
+def test_bad_tile_sizes_are_rejected(ctx):
+    x, y, params = setup_case(100, 64, 1.5, 0.2, 1)
+    for nb in (8, 24, 4096):
+        with pytest.raises(g.GpexError):
+            g.cov_gen(ctx, dev(np.r_[x, y]), 100, params, nb, amp=0)
