@@ -39,41 +39,59 @@ __device__ __forceinline__ double u01(uint32_t lo, uint32_t hi) {
     return ((double)(w >> 11) + 0.5) * (1.0 / 9007199254740992.0);
 }
 
-// N(0,1) value of linear element index l (pair l/2, cosine branch for even l).
-__device__ __forceinline__ double normal_at(uint64_t seed, uint32_t stream, uint64_t l) {
-    uint64_t p = l >> 1;
+// The N(0,1) pair p: elements 2p (cosine branch) and 2p + 1 (sine branch) of the linear index.
+__device__ __forceinline__ void normal_pair(uint64_t seed, uint32_t stream, uint64_t p, double& z0, double& z1) {
     uint32_t x[4] = {(uint32_t)p, (uint32_t)(p >> 32), stream, 0u};
     philox4x32_10(x, (uint32_t)seed, (uint32_t)(seed >> 32));
-    double u1 = u01(x[0], x[1]), u2 = u01(x[2], x[3]);
-    double rad = sqrt(-2.0 * log(u1));
-    double a = 6.283185307179586476925286766559 * u2;
-    return (l & 1) ? rad * sin(a) : rad * cos(a);
+    const double u1 = u01(x[0], x[1]), u2 = u01(x[2], x[3]);
+    const double rad = sqrt(-2.0 * log(u1));
+    double sa, ca;
+    sincos(6.283185307179586476925286766559 * u2, &sa, &ca);
+    z0 = rad * ca;
+    z1 = rad * sa;
 }
 
+// One thread per pair: both elements from one generator call (linear index l = j n + i).
 __global__ void k_normals(uint64_t seed, uint32_t stream, int64_t n, int64_t nsim, double* Z, int64_t ld) {
-    int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= n * nsim) return;
-    int64_t i = idx % n, j = idx / n;
-    Z[i + j * ld] = normal_at(seed, stream, (uint64_t)idx);
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = n * nsim;
+    if (2 * p >= total) return;
+    double z[2];
+    normal_pair(seed, stream, (uint64_t)p, z[0], z[1]);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int64_t l = 2 * p + e;
+        if (l < total) Z[l % n + (l / n) * ld] = z[e];
+    }
 }
 
-// B (rows_pad x cols_pad, leading dim rows_pad): B_ij = Z_ij / s for i < n, j < nsim, else 0,
-// stored in FP16 (RNE) when amp, else FP64.  Per-block partial sums of (Z/s)^2 go to part.
+// B (rows_pad x cols_pad, leading dim rows_pad): B_ij = Z_ij / s for i < n, j < nsim, stored in
+// FP16 (RNE) when amp, else FP64; one thread per element pair of the n x nsim block (linear index
+// l = j n + i).  Per-block partial sums of (Z/s)^2 go to part.  The padding is k_zero_pad's.
 __global__ __launch_bounds__(256) void k_make_B(const double* Zin, int64_t n, int64_t nsim,
-                                                uint64_t seed, int64_t rows_pad, int64_t cols_pad,
-                                                double inv_s, int amp, void* B, double* part) {
-    int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                                                uint64_t seed, int64_t rows_pad, double inv_s, int amp,
+                                                void* B, double* part) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = n * nsim;
     double sq = 0.0;
-    if (idx < rows_pad * cols_pad) {
-        int64_t i = idx % rows_pad, j = idx / rows_pad;
-        double b = 0.0;
-        if (i < n && j < nsim) {
-            double z = Zin ? Zin[i + j * n] : normal_at(seed, 0u, (uint64_t)(j * n + i));
-            b = amp ? z * inv_s : z;
-            sq = b * b;
+    if (2 * p < total) {
+        double z[2];
+        if (Zin) {
+            z[0] = Zin[2 * p];
+            z[1] = 2 * p + 1 < total ? Zin[2 * p + 1] : 0.0;
+        } else {
+            normal_pair(seed, 0u, (uint64_t)p, z[0], z[1]);
         }
-        if (amp) static_cast<_Float16*>(B)[idx] = f64_to_f16(b);
-        else static_cast<double*>(B)[idx] = b;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int64_t l = 2 * p + e;
+            if (l >= total) break;
+            const double b = amp ? z[e] * inv_s : z[e];
+            sq += b * b;
+            const int64_t at = l % n + (l / n) * rows_pad;
+            if (amp) static_cast<_Float16*>(B)[at] = f64_to_f16(b);
+            else static_cast<double*>(B)[at] = b;
+        }
     }
     __shared__ double red[256];
     red[threadIdx.x] = sq;
@@ -83,6 +101,20 @@ __global__ __launch_bounds__(256) void k_make_B(const double* Zin, int64_t n, in
         __syncthreads();
     }
     if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// Zeros of B outside the n x nsim block: rows [n, rows_pad) of every column and every row of
+// columns [nsim, cols_pad).  One thread per element of the padding strip it is launched over.
+__global__ void k_zero_pad(int64_t n, int64_t nsim, int64_t rows_pad, int64_t cols_pad, int amp, void* B) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tail_rows = rows_pad - n;                 // strip 1: (rows_pad - n) x nsim
+    const int64_t n1 = tail_rows * nsim, n2 = rows_pad * (cols_pad - nsim);
+    int64_t at;
+    if (idx < n1) at = n + idx % tail_rows + (idx / tail_rows) * rows_pad;
+    else if (idx < n1 + n2) at = nsim * rows_pad + (idx - n1);   // strip 2: whole padded columns
+    else return;
+    if (amp) static_cast<_Float16*>(B)[at] = (_Float16)0.0f;
+    else static_cast<double*>(B)[at] = 0.0;
 }
 
 // ---- scan ------------------------------------------------------------------------------------
@@ -233,7 +265,8 @@ extern "C" int gpex_normals(gpex_ctx_t ctx, uint64_t seed, uint32_t stream, int6
     if (!d_Z || n < 0 || nsim < 0 || ld < n) return set_err(ctx, GPEX_ERR_ARG, "gpex_normals: bad argument");
     if (n * nsim == 0) return GPEX_OK;
     GPEX_HIP(ctx, hipSetDevice(ctx->device));
-    hipLaunchKernelGGL(k_normals, dim3(blocks(n * nsim)), dim3(256), 0, ctx->stream, seed, stream, n, nsim, d_Z, ld);
+    hipLaunchKernelGGL(k_normals, dim3(blocks((n * nsim + 1) / 2)), dim3(256), 0, ctx->stream, seed, stream, n, nsim,
+                       d_Z, ld);
     GPEX_HIP(ctx, hipGetLastError());
     return GPEX_OK;
 }
@@ -255,7 +288,8 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     double* part = nullptr;
     GemmTask* d_tasks = nullptr;
     auto cleanup = [&]() { dev_free(d_tasks); };
-    const int64_t nblkB = (rows * cols + 255) / 256;
+    const int64_t nblkB = (n * nsim / 2 + 1 + 255) / 256;   // k_make_B: one thread per element pair
+    const int64_t npad = (rows - n) * nsim + rows * (cols - nsim);
     auto al256 = [](size_t b) { return (b + 255) / 256 * 256; };
     const size_t bB = al256((size_t)rows * cols * (amp ? 2 : 8)), bM = al256(sizeof(double) * rows * cols),
                  bP = al256(sizeof(double) * nblkB);
@@ -321,8 +355,10 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         for (auto& e : ev) (void)hipEventCreate(&e);
         (void)hipEventRecord(ev[0], s);
     }
-    hipLaunchKernelGGL(k_make_B, dim3((unsigned)nblkB), dim3(256), 0, s, d_Z, n, nsim, seed, rows, cols,
+    hipLaunchKernelGGL(k_make_B, dim3((unsigned)nblkB), dim3(256), 0, s, d_Z, n, nsim, seed, rows,
                        1.0 / L->s, amp, B, part);
+    if (npad > 0)
+        hipLaunchKernelGGL(k_zero_pad, dim3((unsigned)((npad + 255) / 256)), dim3(256), 0, s, n, nsim, rows, cols, amp, B);
     if (hipGetLastError() != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "make_B launch"); }
     if (ctx->timing) (void)hipEventRecord(ev[1], s);
     if (fused) {
