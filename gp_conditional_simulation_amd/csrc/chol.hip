@@ -150,6 +150,37 @@ __global__ __launch_bounds__(LEAF) void k_potrf_leaf(double* A, int64_t lda, dou
         if (i < n && j < n) T[i + (int64_t)j * ldt] = (j <= i) ? ((i == j ? 1.0 : 0.0) - x[j]) * rii : 0.0;
 }
 
+// End of a halving step: L21 (n2 x n1 in ws, leading dimension n2) into A21, and zeros in the
+// upper-right n1 x n2 blocks of the factor and of its inverse.  blockIdx.y picks the region.
+__global__ void k_join(const double* ws, double* A, int64_t lda, double* T, int64_t ldt, int n1, int n2) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (int64_t)n1 * n2) return;
+    if (blockIdx.y == 0) {
+        const int64_t r = idx % n2, c = idx / n2;                    // L21(r, c)
+        A[n1 + r + c * lda] = ws[idx];
+    } else {
+        const int64_t r = idx % n1, c = n1 + idx / n1;               // upper-right (r, c)
+        if (blockIdx.y == 1) A[r + c * lda] = 0.0;
+        else T[r + c * ldt] = 0.0;
+    }
+}
+
+// Footprint in doubles of the workspace potrf_inv uses for order n: n^2 / 2 (rounded up).
+static int64_t potrf_ws_need(int n) {
+    if (n <= LEAF) return 0;
+    const int n1 = ((n / 2 + 15) / 16) * 16, n2 = n - n1;
+    const int64_t blk = (int64_t)n2 * n1;
+    return std::max(blk, potrf_ws_need(n2)) + blk;
+}
+
+// Factor of the n x n diagonal block A and its inverse T by recursive halving.  Each step:
+//   ws   = A21 T11^T           (L21)
+//   A22 -= ws ws^T
+//   wsb  = ws T11              (kept past the second half: placed beyond its footprint)
+//   join: A21 = ws, upper-right blocks of A and T zeroed
+//   second half on A22
+//   T21  = -T22 wsb
+// ws holds potrf_ws_need(n) doubles (n^2 / 2 suffice).
 int potrf_inv(gpex_ctx_t ctx, hipStream_t s, double* A, int64_t lda, double* T, int64_t ldt, int n,
               double* ws, int64_t col0) {
     auto* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
@@ -163,6 +194,8 @@ int potrf_inv(gpex_ctx_t ctx, hipStream_t s, double* A, int64_t lda, double* T, 
     double* A22 = A + n1 + (int64_t)n1 * lda;
     double* T21 = T + n1;
     double* T22 = T + n1 + (int64_t)n1 * ldt;
+    const int64_t blk = (int64_t)n2 * n1;
+    double* wsb = ws + std::max(blk, potrf_ws_need(n2));
     auto g = [&](const void* a, int tA, int64_t la, const void* b, int tB, int64_t lb, void* c,
                  int64_t lc, int M, int N, int K, double al, double be, int tri) {
         GemmTask t{};
@@ -172,18 +205,17 @@ int potrf_inv(gpex_ctx_t ctx, hipStream_t s, double* A, int64_t lda, double* T, 
         return gemm_launch(ctx, s, DT_F64, nullptr, 1, t);
     };
     GPEX_TRY(potrf_inv(ctx, s, A, lda, T, ldt, n1, ws, col0));
-    // L21 = A21 T11^T (through ws: the product must not overwrite its own input); T11^T is upper
+    // L21 = A21 T11^T into ws (T11^T is upper triangular)
     GPEX_TRY(g(A21, 0, lda, T, 1, ldt, ws, n2, n2, n1, n1, 1.0, 0.0, TRI_B_UPPER));
-    GPEX_TRY(copy2d(ctx, s, ws, DT_F64, n2, A21, DT_F64, lda, n2, n1, 1.0));
     // A22 -= L21 L21^T (only its lower triangle is used)
-    GPEX_TRY(g(A21, 0, lda, A21, 1, lda, A22, lda, n2, n2, n1, -1.0, 1.0, TRI_C_LOWER));
+    GPEX_TRY(g(ws, 0, n2, ws, 1, n2, A22, lda, n2, n2, n1, -1.0, 1.0, TRI_C_LOWER));
+    // wsb = L21 T11
+    GPEX_TRY(g(ws, 0, n2, T, 0, ldt, wsb, n2, n2, n1, n1, 1.0, 0.0, 0));
+    hipLaunchKernelGGL(k_join, dim3((unsigned)((blk + 255) / 256), 3), dim3(256), 0, s, ws, A, lda, T, ldt, n1, n2);
+    GPEX_HIP(ctx, hipGetLastError());
     GPEX_TRY(potrf_inv(ctx, s, A22, lda, T22, ldt, n2, ws, col0 + n1));
-    // T21 = -T22 (L21 T11); T22 is lower
-    GPEX_TRY(g(A21, 0, lda, T, 0, ldt, ws, n2, n2, n1, n1, 1.0, 0.0, 0));
-    GPEX_TRY(g(T22, 0, ldt, ws, 0, n2, T21, ldt, n2, n1, n2, -1.0, 0.0, TRI_A_LOWER));
-    // upper-right blocks of the factor and of its inverse are zero
-    GPEX_TRY(zero2d(ctx, s, A + (int64_t)n1 * lda, lda, n1, n2));
-    GPEX_TRY(zero2d(ctx, s, T + (int64_t)n1 * ldt, ldt, n1, n2));
+    // T21 = -T22 wsb (T22 is lower triangular)
+    GPEX_TRY(g(T22, 0, ldt, wsb, 0, n2, T21, ldt, n2, n1, n2, -1.0, 0.0, TRI_A_LOWER));
     return GPEX_OK;
 }
 
