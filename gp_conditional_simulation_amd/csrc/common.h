@@ -113,8 +113,9 @@ enum : int { TRI_C_LOWER = 1, TRI_A_LOWER = 2, TRI_B_UPPER = 4 };
 // `one` passed by value.  A task whose types differ from `one`'s sets flags[FLAG_BADTASK] and
 // is skipped.
 enum : int { GEMM_GENERIC = 0, GEMM_UPDATE = 1, GEMM_TRMM = 2 };
-extern int g_f16_grid;   // wave grid of FP16 TRMM launches (-1 auto, 0: 2 x 2, 1: 4 x 2, 2: 2 x 4)
-extern int g_gemm_interleave; // typed launches with products and memory instructions interleaved one by one (0 off, 1 on)   // FP64 typed launches with 64 x 128 waves (-1 auto, 0 off, 1 when the shape allows)
+// role only names the kernel symbols (trailing updates, simulation product, the rest) so that
+// kernel traces attribute their time; the launch choices follow the task types.
+extern int g_f16_grid;   // wave grid of FP16 TRMM launches (-1 auto, 0: 2 x 2, otherwise 2 x 4)
 int gemm_launch(gpex_ctx_t ctx, hipStream_t s, int compute, const GemmTask* d_tasks, int ntasks,
                 const GemmTask& one, int role = GEMM_GENERIC);
 

@@ -1,0 +1,592 @@
+// Batched mixed-precision tile GEMM on gfx950 matrix cores: the kernel template and its launch
+// logic, shared by one translation unit per compute precision (gemm_f64.hip, gemm_f32.hip,
+// gemm_f16.hip) so that the three compile in parallel.
+//
+// This is the workhorse of the adaptive mixed-precision tile Cholesky ("Mixed-Precision GPU
+// Acceleration for Confidence Regions of Spatial Excursion Sets", Sec. IV-B: each tile task runs
+// in the precision of its output tile with the operands converted to it), of the panel solves,
+// of kriging (Sec. V-A), of the simulation product (Algorithm 1) and of the conditioning product
+// (Eq. 7).
+//
+// Design (gfx950, wave64):
+//   * A workgroup computes one block of C: 2 x 2 waves of 64 x 64 (128 x 128, 256 threads), or
+//     2 x 4 waves (128 x 256) for large FP16 simulation products.  Each wave's 64 x 64 sub-block
+//     is 4 x 4 matrix-core tiles of 16 x 16, accumulated in vector registers.
+//   * FP64: v_mfma_f64_16x16x4 (lane l, acc r -> row l/16 + 4r, col l%16).
+//     FP32: v_mfma_f32_16x16x4 (row 4(l/16) + r, col l%16).
+//     FP16: v_mfma_f32_16x16x32_f16 with FP32 accumulation (row 4(l/16) + r, col l%16).
+//   * Operand slabs (K = 16 FP64, 32 FP32, 64 FP16) are staged through two LDS buffers and
+//     prefetched two slabs ahead through registers; global loads are coalesced along whichever
+//     index is contiguous in memory and converted on the fly to the compute type (FP64 -> FP16
+//     goes through round-to-odd FP32, which makes the final FP16 rounding a correct
+//     round-to-nearest-even).
+//   * Element types are template parameters; the hot launches (uniform types, and the operand
+//     mixes of the mixed-precision factorization and the simulation product) run fully typed
+//     kernels, and one variant that reads the types from the task at run time covers everything
+//     else (ragged shapes with mixed types, unaligned operands).
+//   * Batched launches place all workgroups of one task on one XCD (workgroups are dealt to the
+//     8 XCDs round-robin by index), so a task's operand tiles stream through a single L2.
+#pragma once
+#include <type_traits>
+#include "common.h"
+#include "devutil.h"
+
+namespace gpex {
+
+typedef double d4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 128, BN = 128, NTHR = 256;
+
+template <typename CT> struct AccT { typedef f4 type; };
+template <> struct AccT<double> { typedef d4 type; };
+
+__device__ __forceinline__ void mma(d4& c, double a, double b) {
+    c = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f4& c, float a, float b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f4& c, h8 a, h8 b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Register fragment of one matrix-core step: one element per lane (FP64/FP32), 8 (FP16).
+template <typename CT> struct FragT { typedef CT type; };
+template <> struct FragT<_Float16> { typedef h8 type; };
+
+// Row of accumulator element r held by lane l inside a 16 x 16 matrix-core tile.
+template <typename CT> __device__ __forceinline__ int acc_row(int l, int r) { return 4 * (l / 16) + r; }
+template <> __device__ __forceinline__ int acc_row<double>(int l, int r) { return l / 16 + 4 * r; }
+
+// Element type tag "read from the task at run time" (operand or output).
+struct DynT {};
+template <typename T> constexpr bool is_dyn = std::is_same<T, DynT>::value;
+
+template <typename T> struct DtOf;
+template <> struct DtOf<double> { static constexpr int v = DT_F64; };
+template <> struct DtOf<float> { static constexpr int v = DT_F32; };
+template <> struct DtOf<_Float16> { static constexpr int v = DT_F16; };
+
+// Whether a task's type code dt is what a kernel built for element type T reads.
+template <typename T> __device__ __forceinline__ bool type_ok(int dt) {
+    if constexpr (is_dyn<T>) return dt == DT_F64 || dt == DT_F32 || dt == DT_F16;
+    else return dt == DtOf<T>::v;
+}
+
+template <typename T> using gptr = const __attribute__((address_space(1))) T*;
+template <typename T> using gptr_mut = __attribute__((address_space(1))) T*;
+
+template <typename CT> struct TCfg;
+template <> struct TCfg<double> { static constexpr int BK = 16, PAD = 2, KSTEP = 4; };
+template <> struct TCfg<float> { static constexpr int BK = 32, PAD = 4, KSTEP = 4; };
+template <> struct TCfg<_Float16> { static constexpr int BK = 64, PAD = 8, KSTEP = 32; };
+
+template <typename CT, typename T> __device__ __forceinline__ CT to_ct(T v);
+template <> __device__ __forceinline__ double to_ct<double, double>(double v) { return v; }
+template <> __device__ __forceinline__ double to_ct<double, float>(float v) { return (double)v; }
+template <> __device__ __forceinline__ double to_ct<double, _Float16>(_Float16 v) { return (double)v; }
+template <> __device__ __forceinline__ float to_ct<float, double>(double v) { return (float)v; }
+template <> __device__ __forceinline__ float to_ct<float, float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_ct<float, _Float16>(_Float16 v) { return (float)v; }
+template <> __device__ __forceinline__ _Float16 to_ct<_Float16, double>(double v) { return f64_to_f16(v); }
+template <> __device__ __forceinline__ _Float16 to_ct<_Float16, float>(float v) { return (_Float16)v; }
+template <> __device__ __forceinline__ _Float16 to_ct<_Float16, _Float16>(_Float16 v) { return v; }
+
+template <typename T, int N> struct VN { typedef T __attribute__((ext_vector_type(N))) type; };
+
+// One operand slab (ROWS rows x BK) of the kernel.  T: the operand's element type in global
+// memory (DynT: read from dt, element by element, ragged-shape kernels only).  CR: the row index
+// is contiguous in global memory.  LDS layout: FP64/FP32 operands with CR are kept as [k][row] (row stride LDR,
+// padded so that the four lane groups of a fragment read hit different banks; stores are plain
+// vector writes); all other operands as [row][k] (k contiguous, the FP16 fragments need 8
+// consecutive k per lane).
+template <typename CT, typename T, bool CR, bool EDGE, int ROWS = 128, int THREADS = NTHR>
+struct TSlab {
+    static constexpr int BK = TCfg<CT>::BK;
+    static constexpr bool KROW = CR && sizeof(CT) >= 4;        // [k][row] layout
+    static constexpr int LDK = BK + TCfg<CT>::PAD;               // [row][k] row stride
+    static constexpr int LDR = ROWS + (sizeof(CT) == 8 ? 4 : 8); // [k][row] k stride
+    static constexpr int ELEMS = KROW ? BK * LDR : ROWS * LDK;
+    // Micro-block path (FP16 compute, row index contiguous): each thread loads MR consecutive rows
+    // in each of KB consecutive k and writes them transposed, KB consecutive k per row, so that the
+    // [row][k] LDS layout the FP16 fragments need is filled with 2 KB-byte stores instead of
+    // 2-byte ones.  Consecutive lanes take consecutive k groups of one row block: their stores
+    // cover a row contiguously (no bank conflicts) and their loads 64-byte column segments.
+    static constexpr bool MB = CR && sizeof(CT) == 2;
+    static constexpr int MR = 8;
+    static constexpr int KB = MB ? ROWS * BK / (MR * THREADS) : 1;
+    static constexpr int KG = BK / KB;                            // k groups per slab (MB)
+    static_assert(!MB || (KB >= 2 && ROWS * BK == MR * KB * THREADS), "micro-blocks must tile the slab");
+    // elements per vector: 16-byte loads for k-contiguous FP16 operands, MR rows on the
+    // micro-block path, else 4 elements
+    static constexpr int VE = MB ? MR : (!CR && sizeof(T) == 2 && sizeof(CT) == 2) ? 8 : 4;
+    static constexpr int VPT = MB ? 1 : (ROWS * BK / THREADS) / VE;
+    static constexpr int TPK = ROWS / VE;                         // threads per k-row (CR)
+    static_assert(MB || (VPT >= 1 && (ROWS * BK) % (THREADS * VE) == 0), "slab must split evenly over the threads");
+    static_assert(EDGE || !is_dyn<T>, "run-time element types are read element by element");
+    CT v[MB ? KB : VPT][VE];
+    int dt = 0;   // element type code of a DynT operand
+
+    // Element i of the operand, converted to the compute type.
+    __device__ __forceinline__ CT get(gptr<T> base, int64_t i) const {
+        if constexpr (is_dyn<T>) {
+            if (dt == DT_F64) return to_ct<CT, double>(((gptr<double>)base)[i]);
+            if (dt == DT_F32) return to_ct<CT, float>(((gptr<float>)base)[i]);
+            return to_ct<CT, _Float16>(((gptr<_Float16>)base)[i]);
+        } else {
+            return to_ct<CT, T>(base[i]);
+        }
+    }
+
+    __device__ __forceinline__ static int idx(int row, int k) { return KROW ? k * LDR + row : row * LDK + k; }
+
+    // Vector q of this thread's share of the slab at (r0, k0), from global memory into registers.
+    __device__ __forceinline__ void load_q(int q, gptr<T> base, int64_t ld, int r0, int k0, int R, int K, int t) {
+        if constexpr (MB) {
+            const int r = (t / KG) * MR, k = (t % KG) * KB;
+            const int gr = r0 + r;
+#pragma unroll
+            for (int kk = 0; kk < KB; ++kk) {
+                const int gk = k0 + k + kk;
+                if constexpr (!EDGE) {
+                    typedef typename VN<T, MR>::type VT;
+                    VT x = *reinterpret_cast<const __attribute__((address_space(1))) VT*>(base + (int64_t)gr + (int64_t)gk * ld);
+#pragma unroll
+                    for (int e = 0; e < MR; ++e) v[kk][e] = to_ct<CT, T>(x[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < MR; ++e)
+                        v[kk][e] = (gr + e < R && gk < K) ? get(base, (int64_t)(gr + e) + (int64_t)gk * ld) : CT(0);
+                }
+            }
+            return;
+        }
+        int r, k;
+        if (CR) {
+            r = (t % TPK) * VE;
+            k = t / TPK + (THREADS / TPK) * q;
+        } else {
+            constexpr int TPR = BK / VE;
+            r = t / TPR + (THREADS / TPR) * q;
+            k = (t % TPR) * VE;
+        }
+        int gr = r0 + r, gk = k0 + k;
+        if constexpr (!EDGE) {
+            int64_t id = CR ? (int64_t)gr + (int64_t)gk * ld : (int64_t)gk + (int64_t)gr * ld;
+            typedef typename VN<T, VE>::type VT;
+            VT x = *reinterpret_cast<const __attribute__((address_space(1))) VT*>(base + id);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) v[q][e] = to_ct<CT, T>(x[e]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                int rr = CR ? gr + e : gr;
+                int kk = CR ? gk : gk + e;
+                v[q][e] = (rr < R && kk < K)
+                              ? get(base, CR ? (int64_t)rr + (int64_t)kk * ld : (int64_t)kk + (int64_t)rr * ld)
+                              : CT(0);
+            }
+        }
+    }
+
+    __device__ __forceinline__ void load(gptr<T> base, int64_t ld, int r0, int k0, int R, int K, int t) {
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) load_q(q, base, ld, r0, k0, R, K, t);
+    }
+
+    // Vector q of the registers into the LDS slab.
+    __device__ __forceinline__ void store_q(int q, CT* sm, int t) {
+        if constexpr (MB) {
+            const int r = (t / KG) * MR, k = (t % KG) * KB;
+            typedef typename VN<CT, KB>::type WT;
+#pragma unroll
+            for (int e = 0; e < MR; ++e) {
+                WT w;
+#pragma unroll
+                for (int kk = 0; kk < KB; ++kk) w[kk] = v[kk][e];
+                *reinterpret_cast<WT*>(&sm[idx(r + e, k)]) = w;
+            }
+            return;
+        }
+        if (CR) {
+            int r = (t % TPK) * VE, k = t / TPK + (THREADS / TPK) * q;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) sm[idx(r + e, k)] = v[q][e];
+        } else {
+            constexpr int TPR = BK / VE;
+            int r = t / TPR + (THREADS / TPR) * q, k = (t % TPR) * VE;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) sm[idx(r, k + e)] = v[q][e];
+        }
+    }
+
+    __device__ __forceinline__ void store(CT* sm, int t) {
+#pragma unroll
+        for (int q = 0; q < VPT; ++q) store_q(q, sm, t);
+    }
+};
+
+// WMW x WNW waves of 64 x (16 FJ) each: a block of (64 WMW) x (16 FJ WNW) outputs per workgroup,
+// two waves per SIMD (accumulators in vector registers: with FJ = 4 they take 128 of them; the
+// run-time-typed variant may drop to one wave per SIMD for the registers its loads need).
+// INTERLEAVE: products and memory instructions issued one by one (whole-block launches).  ROLE
+// only separates the symbols of trailing updates (1) and the simulation product (2) from the
+// other uses (0) so that kernel traces attribute their time.
+template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, bool EDGE, int ROLE,
+          int WMW = 2, int WNW = 2, int FJ = 4, int INTERLEAVE = 0>
+__global__ __launch_bounds__(64 * WMW * WNW)
+__attribute__((amdgpu_waves_per_eu(is_dyn<TA> ? 1 : 2, 2)))
+void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int bmc, int bnc, int xcd_map,
+              unsigned long long* flags) {
+    constexpr int BK = TCfg<CT>::BK;
+    constexpr int TBM = 64 * WMW, WTN = 16 * FJ, TBN = WTN * WNW, THR = 64 * WMW * WNW;
+    constexpr bool a_contig_r = TRA == 0;
+    constexpr bool b_contig_r = TRB != 0;
+    typedef TSlab<CT, TA, a_contig_r, EDGE, TBM, THR> SA;
+    typedef TSlab<CT, TB, b_contig_r, EDGE, TBN, THR> SB;
+    __shared__ __attribute__((aligned(16))) CT As[2][SA::ELEMS];
+    __shared__ __attribute__((aligned(16))) CT Bs[2][SB::ELEMS];
+
+    const int bpt = bmc * bnc;
+    int64_t b = blockIdx.x;
+    int task, blk;
+    if (xcd_map) {
+        int x = (int)(b % 8);
+        int64_t slot = b / 8;
+        task = x + 8 * (int)(slot / bpt);
+        blk = (int)(slot % bpt);
+        if (task >= ntasks) return;
+    } else {
+        task = (int)(b / bpt);
+        blk = (int)(b % bpt);
+    }
+    const GemmTask T = tasks ? tasks[task] : one;
+    if (!type_ok<TA>(T.ta) || !type_ok<TB>(T.tb) || !type_ok<TC>(T.tc) || T.transA != TRA ||
+        (T.transB != 0) != (TRB != 0)) {
+        if (threadIdx.x == 0 && flags) atomicOr(&flags[FLAG_BADTASK], 1ull);
+        return;
+    }
+    gptr<TA> Ap = (gptr<TA>)T.A;
+    gptr<TB> Bp = (gptr<TB>)T.B;
+    const int m0 = (blk % bmc) * TBM, n0 = (blk / bmc) * TBN;
+    if ((T.tri & TRI_C_LOWER) && n0 >= m0 + TBM) return;   // block strictly above the diagonal
+    int kend = T.K;                                        // products beyond kend are exact zeros
+    if (T.tri & TRI_A_LOWER) kend = min(kend, m0 + TBM);
+    if (T.tri & TRI_B_UPPER) kend = min(kend, n0 + TBN);
+    const int t = threadIdx.x, l = t % 64, w = t / 64;
+    const int wm = w % WMW, wn = w / WMW;
+    typedef typename AccT<CT>::type Acc;
+    Acc acc[4][FJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+    SA la;
+    SB lb;
+    la.dt = T.ta;
+    lb.dt = T.tb;
+    const int nk = (kend + BK - 1) / BK;
+    // Operand slabs are prefetched two ahead: slab 0 goes to LDS and slab 1 stays in registers;
+    // during slab kb each register vector is stored into the other LDS buffer (slab kb + 1) and
+    // then reloaded from global memory with slab kb + 2, spread over the slab's steps.
+    la.load(Ap, T.lda, m0, 0, T.M, kend, t);
+    lb.load(Bp, T.ldb, n0, 0, T.N, kend, t);
+    la.store(As[0], t);
+    lb.store(Bs[0], t);
+    if (nk > 1) {
+        la.load(Ap, T.lda, m0, BK, T.M, kend, t);
+        lb.load(Bp, T.ldb, n0, BK, T.N, kend, t);
+    }
+    __syncthreads();
+
+    // Matrix-core steps: 4 k per step for FP64/FP32 (lane group g supplies k = 4 g + e of a 16-k
+    // group), 32 k per step for FP16 (8 consecutive k per lane group).  Fragments are double
+    // buffered in registers: step st + 1 is read from LDS while step st's products run, and at the
+    // end of a slab the next slab's first fragments are read right after the barrier, before the
+    // slab's last products, so the barrier wait does not drain the matrix-core pipe.
+    constexpr int KST = sizeof(CT) == 2 ? 32 : 4;
+    constexpr int NST = BK / KST;
+    static_assert(NST % 2 == 0, "the register double buffer needs an even step count per slab");
+    constexpr int NV = SA::VPT + SB::VPT;   // register vectors per thread per slab
+    constexpr bool IL = INTERLEAVE != 0;
+    typedef typename FragT<CT>::type FT;
+    FT fa[2][4], fb[2][FJ];
+    auto rd = [&](const CT* as, const CT* bs, int st, FT* af, FT* bf) {
+        if constexpr (sizeof(CT) == 2) {
+            const int ks = st * 32;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                af[i] = *reinterpret_cast<const h8*>(&as[SA::idx(wm * 64 + i * 16 + l % 16, ks + 8 * (l / 16))]);
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+                bf[j] = *reinterpret_cast<const h8*>(&bs[SB::idx(wn * WTN + j * 16 + l % 16, ks + 8 * (l / 16))]);
+        } else {
+            const int kk = (st / 4) * 16 + 4 * (l / 16) + st % 4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = as[SA::idx(wm * 64 + i * 16 + l % 16, kk)];
+#pragma unroll
+            for (int j = 0; j < FJ; ++j) bf[j] = bs[SB::idx(wn * WTN + j * 16 + l % 16, kk)];
+        }
+    };
+
+    // One slab.  WR: slab kb + 1 exists (its registers are stored and the barrier is taken);
+    // LD: slab kb + 2 exists (reloaded into the freed registers).  The last two slabs are peeled
+    // off so that every path is straight-line code: the compiler's wait counts then let the
+    // deferred products run while the new fragments are in flight.  Scheduling fences keep the
+    // order per step: next fragments' LDS reads, this step's share of the register vectors
+    // (store, reload), the products; in the last step the barrier and the next slab's first reads
+    // come ahead of the deferred products.
+    auto slab = [&](int kb, auto wr_t, auto ld_t) {
+        constexpr bool WR = decltype(wr_t)::value;
+        constexpr bool LD = decltype(ld_t)::value;
+        const int cur = kb & 1;
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+            const int p = st & 1, q = p ^ 1;
+            if (st + 1 < NST) {
+                rd(As[cur], Bs[cur], st + 1, fa[q], fb[q]);
+                if constexpr (!IL) __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (WR) {
+                // this step's share of the vectors, spread over all but the last step
+#pragma unroll
+                for (int vq = 0; vq < NV; ++vq) {
+                    if (vq * (NST - 1) / NV != st) continue;
+                    if (vq < SA::VPT) {
+                        la.store_q(vq, As[cur ^ 1], t);
+                        if constexpr (LD) la.load_q(vq, Ap, T.lda, m0, (kb + 2) * BK, T.M, kend, t);
+                    } else {
+                        lb.store_q(vq - SA::VPT, Bs[cur ^ 1], t);
+                        if constexpr (LD) lb.load_q(vq - SA::VPT, Bp, T.ldb, n0, (kb + 2) * BK, T.N, kend, t);
+                    }
+                }
+                if (st + 1 == NST) {
+                    __syncthreads();
+                    rd(As[cur ^ 1], Bs[cur ^ 1], 0, fa[q], fb[q]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j) mma(acc[i][j], fb[p][j], fa[p][i]);
+            if constexpr (IL) {
+                // one product, then one LDS or global-memory instruction, in turn
+#pragma unroll
+                for (int g = 0; g < 12; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x0A0, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 4 * FJ, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    rd(As[0], Bs[0], 0, fa[0], fb[0]);
+    for (int kb = 0; kb + 2 < nk; ++kb) slab(kb, std::true_type{}, std::true_type{});
+    if (nk >= 2) slab(nk - 2, std::true_type{}, std::false_type{});
+    slab(nk - 1, std::false_type{}, std::false_type{});
+
+    // Epilogue.  The operands went into the matrix cores as (B, A), so fragment (i, j) holds the
+    // transposed 16 x 16 block: lane l is row l % 16 and register r is column acc_row(l, r).  The 16
+    // lanes of a column then cover 16 consecutive rows of the column-major C (whole cache lines), and
+    // each row group's old C values are all loaded before any store, so their latencies overlap.
+    bool ovf = false;
+    _Float16* __restrict__ C2 = T.C2;
+    const bool use_beta = T.beta != 0.0;
+    auto epilogue = [&](auto out_tag) {   // out_tag: a value of the output element type
+        typedef decltype(out_tag) TO;
+        gptr_mut<TO> Cp = (gptr_mut<TO>)T.C;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + wm * 64 + i * 16 + l % 16;
+            TO cold[FJ][4];
+            if (use_beta) {
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int col = n0 + wn * WTN + j * 16 + acc_row<CT>(l, r);
+                        cold[j][r] = (!EDGE || (row < T.M && col < T.N)) ? Cp[(int64_t)row + (int64_t)col * T.ldc]
+                                                                         : TO(0);
+                    }
+            }
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int col = n0 + wn * WTN + j * 16 + acc_row<CT>(l, r);
+                    if (EDGE && (row >= T.M || col >= T.N)) continue;
+                    const int64_t ci = (int64_t)row + (int64_t)col * T.ldc;
+                    double sv;   // the stored value, exactly, for the optional FP16 copy
+                    if constexpr (sizeof(TO) == 8) {
+                        double v = T.alpha * (double)acc[i][j][r];
+                        if (use_beta) v += T.beta * (double)cold[j][r];
+                        Cp[ci] = v;
+                        sv = v;
+                    } else if constexpr (sizeof(TO) == 4) {
+                        float v = (float)T.alpha * (float)acc[i][j][r];
+                        if (use_beta) v += (float)T.beta * (float)cold[j][r];
+                        Cp[ci] = v;
+                        sv = (double)v;
+                    } else if constexpr (sizeof(CT) == 8) {
+                        double v = T.alpha * acc[i][j][r];
+                        if (use_beta) v += T.beta * (double)cold[j][r];
+                        _Float16 h = f64_to_f16(v);
+                        if (__builtin_isinf((float)h) && !__builtin_isinf(v)) ovf = true;
+                        Cp[ci] = h;
+                        sv = (double)h;
+                    } else {
+                        float v = (float)T.alpha * (float)acc[i][j][r];
+                        if (use_beta) v += (float)T.beta * (float)cold[j][r];
+                        _Float16 h = (_Float16)v;
+                        if (__builtin_isinf((float)h) && !__builtin_isinf(v)) ovf = true;
+                        Cp[ci] = h;
+                        sv = (double)h;
+                    }
+                    if (C2) {
+                        _Float16 h2 = f64_to_f16(sv);
+                        C2[(int64_t)col + (int64_t)row * T.ldc2] = h2;
+                        if (__builtin_isinf((float)h2) && !__builtin_isinf(sv)) ovf = true;
+                    }
+                }
+        }
+    };
+    if constexpr (is_dyn<TC>) {
+        if (T.tc == DT_F64) epilogue(double{});
+        else if (T.tc == DT_F32) epilogue(float{});
+        else epilogue(_Float16{});
+    } else {
+        epilogue(TC{});
+    }
+    if (ovf && flags) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
+}
+
+// Launch the typed kernel when (ta, tb, tc, transA, transB) match; returns 1 if launched.  fast:
+// whole blocks and slabs with aligned operands (vector loads); otherwise the bounds-checked variant
+// runs when RAGGED instantiates it, and the task set goes to the run-time-typed kernel when not.
+template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, int ROLE, bool RAGGED = false>
+static int try_typed(hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one, bool fast,
+                     int64_t grid, int bmc, int bnc, int xcd, unsigned long long* fl) {
+    if (one.ta != DtOf<TA>::v || one.tb != DtOf<TB>::v || one.tc != DtOf<TC>::v) return 0;
+    if (one.transA != TRA || (one.transB != 0) != (TRB != 0)) return 0;
+    if (!fast) {
+        if constexpr (RAGGED) {
+            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, true, ROLE>), dim3((unsigned)grid), dim3(NTHR), 0,
+                               s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+            return 1;
+        }
+        return 0;
+    }
+    if constexpr (sizeof(CT) == 2 && ROLE == GEMM_TRMM && TRA == 1 && TRB == 0) {
+        // 2 x 4 waves (128 x 256 blocks) when that still leaves at least 2048 workgroups
+        const bool wide = one.N % 256 == 0 &&
+                          (g_f16_grid < 0 ? (int64_t)ntasks * (one.M / 128) * (one.N / 256) >= 2048 : g_f16_grid != 0);
+        if (wide) {
+            const int bmc2 = one.M / 128, bnc2 = one.N / 256, bpt2 = bmc2 * bnc2;
+            const int64_t grid2 = xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt2 : (int64_t)ntasks * bpt2;
+            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4, 4, 1>), dim3((unsigned)grid2),
+                               dim3(512), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
+            return 1;
+        }
+    }
+    hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 2, 4, 1>), dim3((unsigned)grid),
+                       dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+    return 1;
+}
+
+// Trailing-update operand mixes of the mixed-precision factorization: C (type CT) -= A B^T with A
+// and B in any of the three tile precisions.
+template <typename CT, typename TA>
+static int try_update_row(hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one, bool fast,
+                          int64_t grid, int bmc, int bnc, int xcd, unsigned long long* fl) {
+    int done = try_typed<CT, TA, double, CT, 0, 1, GEMM_UPDATE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+    if (!done) done = try_typed<CT, TA, float, CT, 0, 1, GEMM_UPDATE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+    if (!done) done = try_typed<CT, TA, _Float16, CT, 0, 1, GEMM_UPDATE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+    return done;
+}
+
+template <typename CT, int ROLE>
+static int launch_ct(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one) {
+    const int M = one.M, N = one.N, K = one.K;
+    if (M <= 0 || N <= 0 || ntasks <= 0) return GPEX_OK;
+    const int bmc = (M + BM - 1) / BM, bnc = (N + BN - 1) / BN;
+    const int bpt = bmc * bnc;
+    const int xcd = ntasks >= 8 ? 1 : 0;
+    const int64_t grid = xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt : (int64_t)ntasks * bpt;
+    if (grid > 0x7fffffffLL) return set_err(ctx, GPEX_ERR_ARG, "gemm grid too large");
+    unsigned long long* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
+    // The vector path needs whole blocks and slabs, leading dimensions that keep 16-byte groups
+    // aligned, and aligned base pointers (checked on the representative task).
+    auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+    const bool fast = (M % BM == 0) && (N % BN == 0) && (K % TCfg<CT>::BK == 0) && (one.lda % 8 == 0) &&
+                      (one.ldb % 8 == 0) && al(one.A) && al(one.B);
+    // uniform types: NT form (trailing updates, panel solves), NN form (simulation product, blocked
+    // solves), TN form (conditioning product W^T R, transposed blocked solves)
+    int done = try_typed<CT, CT, CT, CT, 0, 1, ROLE, true>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+    if (!done) done = try_typed<CT, CT, CT, CT, 0, 0, ROLE, true>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+    if (!done) done = try_typed<CT, CT, CT, CT, 1, 0, ROLE, true>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+    if constexpr (ROLE == GEMM_TRMM && sizeof(CT) == 2) {
+        // simulation product: FP16 row panels (transposed), or tiles of any precision, times FP16 Z/s
+        if (!done) done = try_typed<CT, _Float16, _Float16, double, 1, 0, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+        if (!done) done = try_typed<CT, double, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+        if (!done) done = try_typed<CT, float, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+        if (!done) done = try_typed<CT, _Float16, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+    }
+    if constexpr (ROLE == GEMM_TRMM && sizeof(CT) == 4) {
+        // simulation product, diagonal tiles: FP64 tile times FP16 Z/s in FP32
+        if (!done) done = try_typed<CT, double, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+    }
+    if constexpr (ROLE == GEMM_GENERIC && sizeof(CT) == 8) {
+        // panel solves of reduced-precision tiles: L_ik = A_ik T_kk^T in FP64, stored back in the tile's type
+        if (!done) done = try_typed<CT, float, double, float, 0, 1, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+        if (!done) done = try_typed<CT, _Float16, double, _Float16, 0, 1, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+    }
+    if constexpr (ROLE == GEMM_UPDATE) {
+        if (!done) done = try_update_row<CT, double>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+        if (!done) done = try_update_row<CT, float>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+        if (!done) done = try_update_row<CT, _Float16>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+    }
+    if (!done) {
+        // everything else: element types read from the tasks, bounds-checked element loads
+        switch ((one.transA ? 2 : 0) | (one.transB ? 1 : 0)) {
+            case 0:
+                hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 0, 0, true, GEMM_GENERIC>), dim3((unsigned)grid),
+                                   dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+                break;
+            case 1:
+                hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 0, 1, true, GEMM_GENERIC>), dim3((unsigned)grid),
+                                   dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+                break;
+            case 2:
+                hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 1, 0, true, GEMM_GENERIC>), dim3((unsigned)grid),
+                                   dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+                break;
+            default:
+                hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 1, 1, true, GEMM_GENERIC>), dim3((unsigned)grid),
+                                   dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+                break;
+        }
+    }
+    GPEX_HIP(ctx, hipGetLastError());
+    return GPEX_OK;
+}
+
+// All launches of one compute precision (one translation unit each).
+template <typename CT>
+static int launch_precision(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int ntasks,
+                            const GemmTask& one, int role) {
+    if (role == GEMM_UPDATE) return launch_ct<CT, GEMM_UPDATE>(ctx, s, d_tasks, ntasks, one);
+    if (role == GEMM_TRMM) return launch_ct<CT, GEMM_TRMM>(ctx, s, d_tasks, ntasks, one);
+    return launch_ct<CT, GEMM_GENERIC>(ctx, s, d_tasks, ntasks, one);
+}
+
+int gemm_launch_f64(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one, int role);
+int gemm_launch_f32(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one, int role);
+int gemm_launch_f16(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one, int role);
+
+}  // namespace gpex
