@@ -68,16 +68,27 @@ def hbm_rates(info, n, nsim, t_gen_ms, t_scan_ms):
             "peak_GB_per_s": HBM_GBS}
 
 
+# Sources of the trailing-update kernel and its FP64 launches; the counter summary is valid only
+# for the code it was taken on.
+GEMM_SOURCES = ("gp_conditional_simulation_amd/csrc/gemm_kernel.h", "gp_conditional_simulation_amd/csrc/gemm_f64.hip")
+
+
+def gemm_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_per_launch(prec):
     """HBM bytes per trailing-update launch from the committed counter summary, if it was taken
     on the current GEMM source (else None)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", f"potrf_update_{prec}_unif100k_traffic.json")
-    src = os.path.join(ROOT, "gp_conditional_simulation_amd", "csrc", "gemm.hip")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+    if rec.get("source_sha256") != gemm_source_sha256():
         return None
     return rec.get("traffic_bytes_per_launch")
 

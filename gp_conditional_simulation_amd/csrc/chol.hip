@@ -80,74 +80,122 @@ __global__ void k_copy_tasks(const CopyTask* tasks, int64_t chunk) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Leaf: factor an n x n (n <= 64) FP64 block and invert its factor in one wavefront, without
-// barriers.  Lane i holds row i in registers (rows n..63 are identity padding).
-//   Cholesky, right-looking: at column k the pivot is read from lane k, lane i scales its entry to
-//   l_ik, and every lane updates its row with l_ik l_jk, l_jk read from lane j.
-//   Inverse, forward substitution L X = I by rows: x_i accumulates sum_{q<i} l_iq X_q; row p of
-//   X = (e_p - x_p) / l_pp is final once the rows above it have been applied, and is read from
-//   lane p and applied to the rows below it.
-// Writes L (upper part zeroed) back to A and L^-1 (upper part zeroed) to T.  A non-positive pivot
-// at local column k records col0 + k + 1 in flags[FLAG_INFO] unless an earlier failure is recorded.
-constexpr int LEAF = 64;
+// Leaf: factor an n x n (n <= 128) FP64 block and invert its factor in one pass of one
+// workgroup of 256 threads.  The block is a 16 x 16 grid of 8 x 8 sub-blocks, thread
+// (bi, bj) = (t / 16, t % 16) holding sub-block (bi, bj) in registers; rows and columns n..127 are
+// identity padding.  Column k of the register block is the Schur complement of A while k is
+// ahead of the current step and becomes column k of X = L^-1 once step k has passed, so the
+// factor and its inverse share one set of registers.  Step k (one barrier):
+//   * X update of column k - 1 (right-looking on L X = I): X_ij -= l_i,k-1 X_k-1,j for i > k - 1,
+//     l from the published column, X_k-1 from the published row.
+//   * Pivot l_kk = sqrt(a_kk), read by every thread from the published column k.
+//   * Owners of column k write l_ik = a_ik / l_kk to A and reset their column to e_k (its X part).
+//   * Owners of row k scale X_k,j (j <= k) by 1 / l_kk and publish the row.
+//   * Schur update a_ij -= l_ik l_jk for j > k; the owners of column k + 1 update it first and
+//     publish it for the next step.
+// LDS holds only the published columns (three in flight) and rows (two), so the kernel fits in
+// the registers and LDS one trailing-update workgroup frees and can run beside the update
+// kernel on the look-ahead stream.  Writes L (upper part zeroed) to A and L^-1 (upper part
+// zeroed) to T.  A non-positive pivot at local column k records col0 + k + 1 in
+// flags[FLAG_INFO] unless an earlier failure is recorded.
+constexpr int LEAF = 128;
+constexpr int LEAF_THREADS = 256;
 
-__device__ __forceinline__ double lane_read(double v, int lane) {
-    const int lo = __builtin_amdgcn_readlane(__double2loint(v), lane);
-    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), lane);
-    return __hiloint2double(hi, lo);
-}
-
-__global__ __launch_bounds__(LEAF) void k_potrf_leaf(double* A, int64_t lda, double* T, int64_t ldt,
-                                                     int n, int64_t col0, unsigned long long* flags) {
-    __shared__ double Ls[LEAF][LEAF + 1];
-    const int i = threadIdx.x;
-    double a[LEAF];
+__global__ __launch_bounds__(LEAF_THREADS) void k_potrf_leaf(double* A, int64_t lda, double* T, int64_t ldt,
+                                                             int n, int64_t col0, unsigned long long* flags) {
+    __shared__ __attribute__((aligned(16))) double Lc[3][LEAF];   // column k of the factor (a_ik, unscaled) in slot k % 3
+    __shared__ __attribute__((aligned(16))) double Xr[2][LEAF];   // row k of X in slot k % 2
+    const int t = threadIdx.x, bi = t / 16, bj = t % 16;
+    const int r0 = bi * 8, c0 = bj * 8;
+    double y[8][8];
 #pragma unroll
-    for (int j = 0; j < LEAF; ++j) a[j] = (j <= i && i < n) ? A[i + (int64_t)j * lda] : (i == j ? 1.0 : 0.0);
-    double dii = 1.0;
-    int bad = 0;
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int k = 0; k < LEAF; ++k) {
-        const double akk = lane_read(a[k], k);
-        if (!(akk > 0.0)) {
-            bad = k + 1;
-            break;
+        for (int b = 0; b < 8; ++b) {
+            const int i = r0 + a, j = c0 + b;
+            y[a][b] = (j <= i && i < n) ? A[i + (int64_t)j * lda] : (i == j ? 1.0 : 0.0);
         }
-        const double lkk = sqrt(akk);
-        const double lik = (i > k) ? a[k] / lkk : (i == k ? lkk : 0.0);
-        if (i == k) dii = lkk;
-        a[k] = lik;
+    if (bj == 0) {
 #pragma unroll
-        for (int j = k + 1; j < LEAF; ++j) a[j] -= lik * lane_read(lik, j);
+        for (int a = 0; a < 8; ++a) Lc[0][r0 + a] = y[a][0];
+    }
+    __syncthreads();
+    const int nkb = (n + 7) / 8;
+    double rlp = 0.0;   // 1 / l_k-1,k-1
+    int bad = 0;
+    for (int kb = 0; kb < nkb && !bad; ++kb) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int k = kb * 8 + kk;
+            const double* lc = Lc[k % 3];
+            if (k > 0) {   // X update of column k - 1: independent of this step's pivot
+                const double* lp = Lc[(k + 2) % 3];
+                const double* xp = Xr[(k + 1) & 1];
+                double u[8], v[8];
+#pragma unroll
+                for (int a = 0; a < 8; ++a) u[a] = (r0 + a > k - 1) ? lp[r0 + a] * rlp : 0.0;
+#pragma unroll
+                for (int b = 0; b < 8; ++b) v[b] = xp[c0 + b];
+#pragma unroll
+                for (int a = 0; a < 8; ++a)
+#pragma unroll
+                    for (int b = 0; b < 8; ++b) y[a][b] = fma(-u[a], v[b], y[a][b]);
+            }
+            const double akk = lc[k];   // the same value in every thread: a uniform decision
+            if (!(akk > 0.0)) {
+                bad = k + 1;
+                break;
+            }
+            const double lkk = sqrt(akk), rl = 1.0 / lkk;
+            if (bj == kb) {   // column k of L is final: out to A; the column becomes e_k (its X part)
+#pragma unroll
+                for (int a = 0; a < 8; ++a) {
+                    const int i = r0 + a;
+                    if (i < n && k < n) A[i + (int64_t)k * lda] = i > k ? y[a][kk] * rl : (i == k ? lkk : 0.0);
+                    y[a][kk] = i == k ? 1.0 : 0.0;
+                }
+            }
+            if (bi == kb) {   // row k of X is final up to the division by l_kk
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    const bool xpart = c0 + b <= k;
+                    if (xpart) y[kk][b] *= rl;
+                    Xr[k & 1][c0 + b] = xpart ? y[kk][b] : 0.0;
+                }
+            }
+            double u[8], v[8];
+#pragma unroll
+            for (int a = 0; a < 8; ++a) u[a] = lc[r0 + a] * rl;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) v[b] = (c0 + b > k) ? lc[c0 + b] * rl : 0.0;   // X columns stay
+            const int kn = (kk + 1) % 8;                           // column k + 1 within its sub-block (unrolled: a constant)
+            const int kbn = kb + (kk == 7 ? 1 : 0);
+#pragma unroll
+            for (int a = 0; a < 8; ++a) y[a][kn] = fma(-u[a], v[kn], y[a][kn]);
+            if (bj == kbn) {
+#pragma unroll
+                for (int a = 0; a < 8; ++a) Lc[(k + 1) % 3][r0 + a] = y[a][kn];
+            }
+#pragma unroll
+            for (int a = 0; a < 8; ++a)
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    if (b != kn) y[a][b] = fma(-u[a], v[b], y[a][b]);
+            rlp = rl;
+            __syncthreads();
+        }
     }
     if (bad) {
-        if (i == 0 && flags) atomicCAS(&flags[FLAG_INFO], 0ull, (unsigned long long)(col0 + bad));
+        if (t == 0 && flags) atomicCAS(&flags[FLAG_INFO], 0ull, (unsigned long long)(col0 + bad));
         return;
     }
 #pragma unroll
-    for (int j = 0; j < LEAF; ++j) {
-        const double v = (j <= i) ? a[j] : 0.0;
-        Ls[i][j] = v;
-        if (i < n && j < n) A[i + (int64_t)j * lda] = v;
-    }
-    // Ls row i is only read back by lane i itself: no barrier is needed
-    const double rii = 1.0 / dii;
-    double x[LEAF];
+    for (int a = 0; a < 8; ++a)
 #pragma unroll
-    for (int j = 0; j < LEAF; ++j) x[j] = 0.0;
-#pragma unroll
-    for (int p = 0; p < LEAF - 1; ++p) {
-        const double rpp = lane_read(rii, p);
-        const double lip = (i > p) ? Ls[i][p] : 0.0;   // rows at or above p receive exact zeros
-#pragma unroll
-        for (int j = 0; j <= p; ++j) {
-            const double xpj = ((p == j ? 1.0 : 0.0) - lane_read(x[j], p)) * rpp;   // X[p][j]
-            x[j] += lip * xpj;
+        for (int b = 0; b < 8; ++b) {
+            const int i = r0 + a, j = c0 + b;
+            if (i < n && j < n) T[i + (int64_t)j * ldt] = j <= i ? y[a][b] : 0.0;
         }
-    }
-#pragma unroll
-    for (int j = 0; j < LEAF; ++j)
-        if (i < n && j < n) T[i + (int64_t)j * ldt] = (j <= i) ? ((i == j ? 1.0 : 0.0) - x[j]) * rii : 0.0;
 }
 
 // End of a halving step: L21 (n2 x n1 in ws, leading dimension n2) into A21, and zeros in the
@@ -185,7 +233,7 @@ int potrf_inv(gpex_ctx_t ctx, hipStream_t s, double* A, int64_t lda, double* T, 
               double* ws, int64_t col0) {
     auto* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
     if (n <= LEAF) {
-        hipLaunchKernelGGL(k_potrf_leaf, dim3(1), dim3(LEAF), 0, s, A, lda, T, ldt, n, col0, fl);
+        hipLaunchKernelGGL(k_potrf_leaf, dim3(1), dim3(LEAF_THREADS), 0, s, A, lda, T, ldt, n, col0, fl);
         GPEX_HIP(ctx, hipGetLastError());
         return GPEX_OK;
     }
