@@ -62,6 +62,12 @@ extern "C" int gpex_ctx_destroy(gpex_ctx_t ctx) {
     else (void)hipDeviceSynchronize();
     dev_free(ctx->d_flags);
     dev_free(ctx->sim_ws);
+    if (ctx->side) {
+        (void)hipStreamSynchronize(ctx->side);
+        (void)hipStreamDestroy(ctx->side);
+    }
+    if (ctx->side_fork) (void)hipEventDestroy(ctx->side_fork);
+    if (ctx->side_join) (void)hipEventDestroy(ctx->side_join);
     delete ctx;
     return GPEX_OK;
 }

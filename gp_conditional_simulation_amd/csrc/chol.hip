@@ -4,8 +4,8 @@
 // Sec. IV-B and Algorithm 2 (step 12): the scaled covariance s^2 V, cut into nb x nb tiles with a
 // per-tile precision map, is factored right-looking.  Step k:
 //   * diagonal tile (k, k): FP64 POTRF.  Here it is factored together with its explicit inverse
-//     T_k = L_kk^-1 by recursive halving down to a single-wavefront 64 x 64 leaf (register resident);
-//     the halves are joined with FP64 matrix-core GEMMs.
+//     T_k = L_kk^-1 by recursive halving down to leaves of order <= 128 (factor and inverse in one
+//     pass of one workgroup); the halves are joined with FP64 matrix-core GEMMs.
 //   * panel tiles (i, k), i > k: L_ik = A_ik L_kk^-T evaluated as the product A_ik T_k^T on FP64
 //     matrix cores for every tile and rounded once to the tile's storage precision (one batched
 //     launch).  An FP32 product through the explicit inverse carries an error of about

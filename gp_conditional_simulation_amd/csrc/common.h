@@ -30,6 +30,10 @@ struct gpex_ctx_s {
     // grown when a call needs more
     void* sim_ws = nullptr;
     size_t sim_ws_bytes = 0;
+    // side stream (default priority) for the ragged strips of a split GEMM launch, forked from and
+    // joined to the launching stream through two events; created on first use
+    hipStream_t side = nullptr;
+    hipEvent_t side_fork = nullptr, side_join = nullptr;
 };
 
 struct gpex_tiled_s {

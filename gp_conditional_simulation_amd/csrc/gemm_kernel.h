@@ -229,6 +229,9 @@ struct TSlab {
     }
 };
 
+// A launch covers bmc x bnc blocks of every task, the block grid starting at row m_off and column
+// n_off of C (a launch may cover only part of C: the whole-block part and its ragged strips go to
+// separate launches).
 // WMW x WNW waves of 64 x (16 FJ) each: a block of (64 WMW) x (16 FJ WNW) outputs per workgroup,
 // two waves per SIMD (accumulators in vector registers: with FJ = 4 they take 128 of them; the
 // run-time-typed variant may drop to one wave per SIMD for the registers its loads need).
@@ -239,8 +242,8 @@ template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, 
           int WMW = 2, int WNW = 2, int FJ = 4, int INTERLEAVE = 0>
 __global__ __launch_bounds__(64 * WMW * WNW)
 __attribute__((amdgpu_waves_per_eu(is_dyn<TA> ? 1 : 2, 2)))
-void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int bmc, int bnc, int xcd_map,
-              unsigned long long* flags) {
+void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int bmc, int bnc, int m_off,
+              int n_off, int xcd_map, unsigned long long* flags) {
     constexpr int BK = TCfg<CT>::BK;
     constexpr int TBM = 64 * WMW, WTN = 16 * FJ, TBN = WTN * WNW, THR = 64 * WMW * WNW;
     constexpr bool a_contig_r = TRA == 0;
@@ -271,7 +274,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     }
     gptr<TA> Ap = (gptr<TA>)T.A;
     gptr<TB> Bp = (gptr<TB>)T.B;
-    const int m0 = (blk % bmc) * TBM, n0 = (blk / bmc) * TBN;
+    const int m0 = m_off + (blk % bmc) * TBM, n0 = n_off + (blk / bmc) * TBN;   // block origin in the task
     if ((T.tri & TRI_C_LOWER) && n0 >= m0 + TBM) return;   // block strictly above the diagonal
     int kend = T.K;                                        // products beyond kend are exact zeros
     if (T.tri & TRI_A_LOWER) kend = min(kend, m0 + TBM);
@@ -466,48 +469,116 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     if (ovf && flags) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
 }
 
-// Launch the typed kernel when (ta, tb, tc, transA, transB) match; returns 1 if launched.  fast:
-// whole blocks and slabs with aligned operands (vector loads); otherwise the bounds-checked variant
-// runs when RAGGED instantiates it, and the task set goes to the run-time-typed kernel when not.
+// Part of the output of a launch: bmc x bnc blocks of 128 x 128 from (m_off, n_off), in every task.
+struct Part {
+    int m_off, n_off, bmc, bnc;
+    bool fast;   // whole blocks and slabs with aligned operands: vector loads, no bounds checks
+};
+
+static int64_t part_grid(const Part& p, int ntasks, int xcd) {
+    const int64_t bpt = (int64_t)p.bmc * p.bnc;
+    return xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt : (int64_t)ntasks * bpt;
+}
+
+// Launch the typed kernel on one part when (ta, tb, tc, transA, transB) match; returns 1 if
+// launched.  A part that needs bounds checks runs the bounds-checked variant when RAGGED
+// instantiates it, and otherwise returns 0 (the run-time-typed kernel takes it).
 template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, int ROLE, bool RAGGED = false>
-static int try_typed(hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one, bool fast,
-                     int64_t grid, int bmc, int bnc, int xcd, unsigned long long* fl) {
+static int try_typed(hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one, const Part& p, int xcd,
+                     unsigned long long* fl) {
     if (one.ta != DtOf<TA>::v || one.tb != DtOf<TB>::v || one.tc != DtOf<TC>::v) return 0;
     if (one.transA != TRA || (one.transB != 0) != (TRB != 0)) return 0;
-    if (!fast) {
+    const unsigned grid = (unsigned)part_grid(p, ntasks, xcd);
+    if (!p.fast) {
         if constexpr (RAGGED) {
-            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, true, ROLE>), dim3((unsigned)grid), dim3(NTHR), 0,
-                               s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, true, ROLE>), dim3(grid), dim3(NTHR), 0, s, d_tasks,
+                               one, ntasks, p.bmc, p.bnc, p.m_off, p.n_off, xcd, fl);
             return 1;
         }
         return 0;
     }
     if constexpr (sizeof(CT) == 2 && ROLE == GEMM_TRMM && TRA == 1 && TRB == 0) {
-        // 2 x 4 waves (128 x 256 blocks) when that still leaves at least 2048 workgroups
-        const bool wide = one.N % 256 == 0 &&
+        // 2 x 4 waves (128 x 256 blocks) when the part is all of C and that still leaves at least
+        // 2048 workgroups
+        const bool whole = p.m_off == 0 && p.n_off == 0 && p.bmc * 128 == one.M && p.bnc * 128 == one.N;
+        const bool wide = whole && one.N % 256 == 0 &&
                           (g_f16_grid < 0 ? (int64_t)ntasks * (one.M / 128) * (one.N / 256) >= 2048 : g_f16_grid != 0);
         if (wide) {
-            const int bmc2 = one.M / 128, bnc2 = one.N / 256, bpt2 = bmc2 * bnc2;
-            const int64_t grid2 = xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt2 : (int64_t)ntasks * bpt2;
-            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4, 4, 1>), dim3((unsigned)grid2),
-                               dim3(512), 0, s, d_tasks, one, ntasks, bmc2, bnc2, xcd, fl);
+            const Part w{0, 0, one.M / 128, one.N / 256, true};
+            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4, 4, 1>),
+                               dim3((unsigned)part_grid(w, ntasks, xcd)), dim3(512), 0, s, d_tasks, one, ntasks, w.bmc,
+                               w.bnc, 0, 0, xcd, fl);
             return 1;
         }
     }
-    hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 2, 4, 1>), dim3((unsigned)grid),
-                       dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
+    hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 2, 4, 1>), dim3(grid), dim3(NTHR), 0, s,
+                       d_tasks, one, ntasks, p.bmc, p.bnc, p.m_off, p.n_off, xcd, fl);
     return 1;
 }
 
 // Trailing-update operand mixes of the mixed-precision factorization: C (type CT) -= A B^T with A
 // and B in any of the three tile precisions.
 template <typename CT, typename TA>
-static int try_update_row(hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one, bool fast,
-                          int64_t grid, int bmc, int bnc, int xcd, unsigned long long* fl) {
-    int done = try_typed<CT, TA, double, CT, 0, 1, GEMM_UPDATE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-    if (!done) done = try_typed<CT, TA, float, CT, 0, 1, GEMM_UPDATE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-    if (!done) done = try_typed<CT, TA, _Float16, CT, 0, 1, GEMM_UPDATE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
+static int try_update_row(hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one, const Part& p,
+                          int xcd, unsigned long long* fl) {
+    int done = try_typed<CT, TA, double, CT, 0, 1, GEMM_UPDATE>(s, d_tasks, ntasks, one, p, xcd, fl);
+    if (!done) done = try_typed<CT, TA, float, CT, 0, 1, GEMM_UPDATE>(s, d_tasks, ntasks, one, p, xcd, fl);
+    if (!done) done = try_typed<CT, TA, _Float16, CT, 0, 1, GEMM_UPDATE>(s, d_tasks, ntasks, one, p, xcd, fl);
     return done;
+}
+
+// One part of a launch: the typed kernel of the task signature if there is one, else the
+// run-time-typed kernel.
+template <typename CT, int ROLE>
+static void launch_part(hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one, const Part& p,
+                        int xcd, unsigned long long* fl) {
+    // uniform types: NT form (trailing updates, panel solves), NN form (simulation product, blocked
+    // solves), TN form (conditioning product W^T R, transposed blocked solves)
+    int done = try_typed<CT, CT, CT, CT, 0, 1, ROLE, true>(s, d_tasks, ntasks, one, p, xcd, fl);
+    if (!done) done = try_typed<CT, CT, CT, CT, 0, 0, ROLE, true>(s, d_tasks, ntasks, one, p, xcd, fl);
+    if (!done) done = try_typed<CT, CT, CT, CT, 1, 0, ROLE, true>(s, d_tasks, ntasks, one, p, xcd, fl);
+    if constexpr (ROLE == GEMM_TRMM && sizeof(CT) == 2) {
+        // simulation product: FP16 row panels (transposed), or tiles of any precision, times FP16 Z/s
+        if (!done) done = try_typed<CT, _Float16, _Float16, double, 1, 0, ROLE>(s, d_tasks, ntasks, one, p, xcd, fl);
+        if (!done) done = try_typed<CT, double, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, p, xcd, fl);
+        if (!done) done = try_typed<CT, float, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, p, xcd, fl);
+        if (!done) done = try_typed<CT, _Float16, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, p, xcd, fl);
+    }
+    if constexpr (ROLE == GEMM_TRMM && sizeof(CT) == 4) {
+        // simulation product, diagonal tiles: FP64 tile times FP16 Z/s in FP32
+        if (!done) done = try_typed<CT, double, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, p, xcd, fl);
+    }
+    if constexpr (ROLE == GEMM_GENERIC && sizeof(CT) == 8) {
+        // panel solves of reduced-precision tiles: L_ik = A_ik T_kk^T in FP64, stored back in the tile's type
+        if (!done) done = try_typed<CT, float, double, float, 0, 1, ROLE>(s, d_tasks, ntasks, one, p, xcd, fl);
+        if (!done) done = try_typed<CT, _Float16, double, _Float16, 0, 1, ROLE>(s, d_tasks, ntasks, one, p, xcd, fl);
+    }
+    if constexpr (ROLE == GEMM_UPDATE) {
+        if (!done) done = try_update_row<CT, double>(s, d_tasks, ntasks, one, p, xcd, fl);
+        if (!done) done = try_update_row<CT, float>(s, d_tasks, ntasks, one, p, xcd, fl);
+        if (!done) done = try_update_row<CT, _Float16>(s, d_tasks, ntasks, one, p, xcd, fl);
+    }
+    if (done) return;
+    // everything else: element types read from the tasks, bounds-checked element loads
+    const dim3 grid((unsigned)part_grid(p, ntasks, xcd));
+    switch ((one.transA ? 2 : 0) | (one.transB ? 1 : 0)) {
+        case 0:
+            hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 0, 0, true, GEMM_GENERIC>), grid, dim3(NTHR), 0, s, d_tasks,
+                               one, ntasks, p.bmc, p.bnc, p.m_off, p.n_off, xcd, fl);
+            break;
+        case 1:
+            hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 0, 1, true, GEMM_GENERIC>), grid, dim3(NTHR), 0, s, d_tasks,
+                               one, ntasks, p.bmc, p.bnc, p.m_off, p.n_off, xcd, fl);
+            break;
+        case 2:
+            hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 1, 0, true, GEMM_GENERIC>), grid, dim3(NTHR), 0, s, d_tasks,
+                               one, ntasks, p.bmc, p.bnc, p.m_off, p.n_off, xcd, fl);
+            break;
+        default:
+            hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 1, 1, true, GEMM_GENERIC>), grid, dim3(NTHR), 0, s, d_tasks,
+                               one, ntasks, p.bmc, p.bnc, p.m_off, p.n_off, xcd, fl);
+            break;
+    }
 }
 
 template <typename CT, int ROLE>
@@ -515,62 +586,38 @@ static int launch_ct(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
     const int M = one.M, N = one.N, K = one.K;
     if (M <= 0 || N <= 0 || ntasks <= 0) return GPEX_OK;
     const int bmc = (M + BM - 1) / BM, bnc = (N + BN - 1) / BN;
-    const int bpt = bmc * bnc;
     const int xcd = ntasks >= 8 ? 1 : 0;
-    const int64_t grid = xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt : (int64_t)ntasks * bpt;
-    if (grid > 0x7fffffffLL) return set_err(ctx, GPEX_ERR_ARG, "gemm grid too large");
+    if (part_grid(Part{0, 0, bmc, bnc, false}, ntasks, xcd) > 0x7fffffffLL)
+        return set_err(ctx, GPEX_ERR_ARG, "gemm grid too large");
     unsigned long long* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
-    // The vector path needs whole blocks and slabs, leading dimensions that keep 16-byte groups
-    // aligned, and aligned base pointers (checked on the representative task).
+    // The vector path needs whole slabs, leading dimensions that keep 16-byte groups aligned, and
+    // aligned base pointers (checked on the representative task).  When only M or N is ragged, the
+    // whole 128-blocks run the vector path and the leftover strips (fewer than 128 rows at the
+    // bottom, fewer than 128 columns at the right) the bounds-checked one.
     auto al = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
-    const bool fast = (M % BM == 0) && (N % BN == 0) && (K % TCfg<CT>::BK == 0) && (one.lda % 8 == 0) &&
-                      (one.ldb % 8 == 0) && al(one.A) && al(one.B);
-    // uniform types: NT form (trailing updates, panel solves), NN form (simulation product, blocked
-    // solves), TN form (conditioning product W^T R, transposed blocked solves)
-    int done = try_typed<CT, CT, CT, CT, 0, 1, ROLE, true>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-    if (!done) done = try_typed<CT, CT, CT, CT, 0, 0, ROLE, true>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-    if (!done) done = try_typed<CT, CT, CT, CT, 1, 0, ROLE, true>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-    if constexpr (ROLE == GEMM_TRMM && sizeof(CT) == 2) {
-        // simulation product: FP16 row panels (transposed), or tiles of any precision, times FP16 Z/s
-        if (!done) done = try_typed<CT, _Float16, _Float16, double, 1, 0, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-        if (!done) done = try_typed<CT, double, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-        if (!done) done = try_typed<CT, float, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-        if (!done) done = try_typed<CT, _Float16, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-    }
-    if constexpr (ROLE == GEMM_TRMM && sizeof(CT) == 4) {
-        // simulation product, diagonal tiles: FP64 tile times FP16 Z/s in FP32
-        if (!done) done = try_typed<CT, double, _Float16, double, 0, 0, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-    }
-    if constexpr (ROLE == GEMM_GENERIC && sizeof(CT) == 8) {
-        // panel solves of reduced-precision tiles: L_ik = A_ik T_kk^T in FP64, stored back in the tile's type
-        if (!done) done = try_typed<CT, float, double, float, 0, 1, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-        if (!done) done = try_typed<CT, _Float16, double, _Float16, 0, 1, ROLE>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-    }
-    if constexpr (ROLE == GEMM_UPDATE) {
-        if (!done) done = try_update_row<CT, double>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-        if (!done) done = try_update_row<CT, float>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-        if (!done) done = try_update_row<CT, _Float16>(s, d_tasks, ntasks, one, fast, grid, bmc, bnc, xcd, fl);
-    }
-    if (!done) {
-        // everything else: element types read from the tasks, bounds-checked element loads
-        switch ((one.transA ? 2 : 0) | (one.transB ? 1 : 0)) {
-            case 0:
-                hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 0, 0, true, GEMM_GENERIC>), dim3((unsigned)grid),
-                                   dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
-                break;
-            case 1:
-                hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 0, 1, true, GEMM_GENERIC>), dim3((unsigned)grid),
-                                   dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
-                break;
-            case 2:
-                hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 1, 0, true, GEMM_GENERIC>), dim3((unsigned)grid),
-                                   dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
-                break;
-            default:
-                hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 1, 1, true, GEMM_GENERIC>), dim3((unsigned)grid),
-                                   dim3(NTHR), 0, s, d_tasks, one, ntasks, bmc, bnc, xcd, fl);
-                break;
+    const bool kfast = (K % TCfg<CT>::BK == 0) && (one.lda % 8 == 0) && (one.ldb % 8 == 0) && al(one.A) && al(one.B);
+    const int mw = kfast ? M / BM : 0, nw = kfast ? N / BN : 0;   // whole block rows / columns
+    if (mw == bmc && nw == bnc) {
+        launch_part<CT, ROLE>(s, d_tasks, ntasks, one, Part{0, 0, mw, nw, true}, xcd, fl);
+    } else if ((int64_t)mw * nw * ntasks < 1024) {
+        // few whole blocks: one bounds-checked launch costs less than three on the critical path
+        launch_part<CT, ROLE>(s, d_tasks, ntasks, one, Part{0, 0, bmc, bnc, false}, xcd, fl);
+    } else {
+        // the strips run beside the whole blocks on the context's side stream
+        if (!ctx->side) {
+            GPEX_HIP(ctx, hipStreamCreateWithFlags(&ctx->side, hipStreamNonBlocking));
+            GPEX_HIP(ctx, hipEventCreateWithFlags(&ctx->side_fork, hipEventDisableTiming));
+            GPEX_HIP(ctx, hipEventCreateWithFlags(&ctx->side_join, hipEventDisableTiming));
         }
+        GPEX_HIP(ctx, hipEventRecord(ctx->side_fork, s));
+        GPEX_HIP(ctx, hipStreamWaitEvent(ctx->side, ctx->side_fork, 0));
+        if (mw < bmc)   // bottom strip, every column
+            launch_part<CT, ROLE>(ctx->side, d_tasks, ntasks, one, Part{mw * BM, 0, 1, bnc, false}, xcd, fl);
+        if (nw < bnc)   // right strip, the whole block rows
+            launch_part<CT, ROLE>(ctx->side, d_tasks, ntasks, one, Part{0, nw * BN, mw, 1, false}, xcd, fl);
+        GPEX_HIP(ctx, hipEventRecord(ctx->side_join, ctx->side));
+        launch_part<CT, ROLE>(s, d_tasks, ntasks, one, Part{0, 0, mw, nw, true}, xcd, fl);
+        GPEX_HIP(ctx, hipStreamWaitEvent(s, ctx->side_join, 0));
     }
     GPEX_HIP(ctx, hipGetLastError());
     return GPEX_OK;
