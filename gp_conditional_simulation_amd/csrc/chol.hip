@@ -93,6 +93,7 @@ __global__ void k_copy_tasks(const CopyTask* tasks, int64_t chunk) {
 //   * Owners of row k scale X_k,j (j <= k) by 1 / l_kk and publish the row.
 //   * Schur update a_ij -= l_ik l_jk for j > k; the owners of column k + 1 update it first and
 //     publish it for the next step.
+// The per-column barrier orders LDS only: the stores of L to A are not waited for.
 // LDS holds only the published columns (three in flight) and rows (two), so the kernel fits in
 // the registers and LDS one trailing-update workgroup frees and can run beside the update
 // kernel on the look-ahead stream.  Writes L (upper part zeroed) to A and L^-1 (upper part
@@ -100,6 +101,14 @@ __global__ void k_copy_tasks(const CopyTask* tasks, int64_t chunk) {
 // flags[FLAG_INFO] unless an earlier failure is recorded.
 constexpr int LEAF = 128;
 constexpr int LEAF_THREADS = 256;
+
+// Workgroup barrier that orders LDS accesses only.  The leaf's global stores of L need no
+// ordering against the other threads, and a full barrier would wait for them at every column.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __global__ __launch_bounds__(LEAF_THREADS) void k_potrf_leaf(double* A, int64_t lda, double* T, int64_t ldt,
                                                              int n, int64_t col0, unsigned long long* flags) {
@@ -182,7 +191,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void k_potrf_leaf(double* A, int64_t 
                 for (int b = 0; b < 8; ++b)
                     if (b != kn) y[a][b] = fma(-u[a], v[b], y[a][b]);
             rlp = rl;
-            __syncthreads();
+            lds_barrier();
         }
     }
     if (bad) {
