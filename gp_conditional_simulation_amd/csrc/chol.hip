@@ -85,15 +85,16 @@ __global__ void k_copy_tasks(const CopyTask* tasks, int64_t chunk) {
 // (bi, bj) = (t / 16, t % 16) holding sub-block (bi, bj) in registers; rows and columns n..127 are
 // identity padding.  Column k of the register block is the Schur complement of A while k is
 // ahead of the current step and becomes column k of X = L^-1 once step k has passed, so the
-// factor and its inverse share one set of registers.  Step k (one barrier):
-//   * X update of column k - 1 (right-looking on L X = I): X_ij -= l_i,k-1 X_k-1,j for i > k - 1,
-//     l from the published column, X_k-1 from the published row.
-//   * Pivot l_kk = sqrt(a_kk), read by every thread from the published column k.
-//   * Owners of column k write l_ik = a_ik / l_kk to A and reset their column to e_k (its X part).
-//   * Owners of row k scale X_k,j (j <= k) by 1 / l_kk and publish the row.
-//   * Schur update a_ij -= l_ik l_jk for j > k; the owners of column k + 1 update it first and
-//     publish it for the next step.
-// The per-column barrier orders LDS only: the stores of L to A are not waited for.
+// factor and its inverse share one set of registers.
+// Column k of the Schur complement is published before step k with its pivot a_kk in a slot of
+// its own and zeros on and above the diagonal, so that no update needs a mask.  Step k (one
+// barrier, which orders LDS only):
+//   * X update of column k - 1 (right-looking on L X = I): X_ij -= l_i,k-1 X_k-1,j, i > k - 1.
+//   * Pivot: 1 / l_kk from the hardware reciprocal square root and two Newton steps.
+//   * Schur update a_ij -= (a_ik / a_kk) a_jk for i, j > k; the owners of column k + 1 update it
+//     first and publish it.
+//   * Owners of column k reset it to e_k (its X part); owners of row k scale X_k,j (j <= k) by
+//     1 / l_kk and publish the row; threads 0..127 store column k of L = a_ik / l_kk to A.
 // LDS holds only the published columns (three in flight) and rows (two), so the kernel fits in
 // the registers and LDS one trailing-update workgroup frees and can run beside the update
 // kernel on the look-ahead stream.  Writes L (upper part zeroed) to A and L^-1 (upper part
@@ -112,8 +113,9 @@ __device__ __forceinline__ void lds_barrier() {
 
 __global__ __launch_bounds__(LEAF_THREADS) void k_potrf_leaf(double* A, int64_t lda, double* T, int64_t ldt,
                                                              int n, int64_t col0, unsigned long long* flags) {
-    __shared__ __attribute__((aligned(16))) double Lc[3][LEAF];   // column k of the factor (a_ik, unscaled) in slot k % 3
-    __shared__ __attribute__((aligned(16))) double Xr[2][LEAF];   // row k of X in slot k % 2
+    __shared__ __attribute__((aligned(16))) double Lc[3][LEAF];   // a_ik below the diagonal, column k in slot k % 3
+    __shared__ double Pv[3];                                      // a_kk in slot k % 3
+    __shared__ __attribute__((aligned(16))) double Xr[2][LEAF];   // row k of X (zero beyond k) in slot k % 2
     const int t = threadIdx.x, bi = t / 16, bj = t % 16;
     const int r0 = bi * 8, c0 = bj * 8;
     double y[8][8];
@@ -126,7 +128,8 @@ __global__ __launch_bounds__(LEAF_THREADS) void k_potrf_leaf(double* A, int64_t 
         }
     if (bj == 0) {
 #pragma unroll
-        for (int a = 0; a < 8; ++a) Lc[0][r0 + a] = y[a][0];
+        for (int a = 0; a < 8; ++a) Lc[0][r0 + a] = r0 + a > 0 ? y[a][0] : 0.0;
+        if (bi == 0) Pv[0] = y[0][0];
     }
     __syncthreads();
     const int nkb = (n + 7) / 8;
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void k_potrf_leaf(double* A, int64_t 
                 const double* xp = Xr[(k + 1) & 1];
                 double u[8], v[8];
 #pragma unroll
-                for (int a = 0; a < 8; ++a) u[a] = (r0 + a > k - 1) ? lp[r0 + a] * rlp : 0.0;
+                for (int a = 0; a < 8; ++a) u[a] = lp[r0 + a] * rlp;
 #pragma unroll
                 for (int b = 0; b < 8; ++b) v[b] = xp[c0 + b];
 #pragma unroll
@@ -150,46 +153,47 @@ __global__ __launch_bounds__(LEAF_THREADS) void k_potrf_leaf(double* A, int64_t 
 #pragma unroll
                     for (int b = 0; b < 8; ++b) y[a][b] = fma(-u[a], v[b], y[a][b]);
             }
-            const double akk = lc[k];   // the same value in every thread: a uniform decision
+            const double akk = Pv[k % 3];   // the same value in every thread: a uniform decision
             if (!(akk > 0.0)) {
                 bad = k + 1;
                 break;
             }
-            const double lkk = sqrt(akk), rl = 1.0 / lkk;
-            if (bj == kb) {   // column k of L is final: out to A; the column becomes e_k (its X part)
-#pragma unroll
-                for (int a = 0; a < 8; ++a) {
-                    const int i = r0 + a;
-                    if (i < n && k < n) A[i + (int64_t)k * lda] = i > k ? y[a][kk] * rl : (i == k ? lkk : 0.0);
-                    y[a][kk] = i == k ? 1.0 : 0.0;
-                }
-            }
-            if (bi == kb) {   // row k of X is final up to the division by l_kk
-#pragma unroll
-                for (int b = 0; b < 8; ++b) {
-                    const bool xpart = c0 + b <= k;
-                    if (xpart) y[kk][b] *= rl;
-                    Xr[k & 1][c0 + b] = xpart ? y[kk][b] : 0.0;
-                }
-            }
+            double rl = __builtin_amdgcn_rsq(akk);   // refined to 1 / sqrt(a_kk) by two Newton steps
+            rl = fma(0.5 * rl, fma(-akk * rl, rl, 1.0), rl);
+            rl = fma(0.5 * rl, fma(-akk * rl, rl, 1.0), rl);
+            const double lkk = akk * rl, rk = rl * rl;
+            // Schur update with column k; column k + 1 first, then published
             double u[8], v[8];
 #pragma unroll
-            for (int a = 0; a < 8; ++a) u[a] = lc[r0 + a] * rl;
+            for (int a = 0; a < 8; ++a) u[a] = lc[r0 + a] * rk;
 #pragma unroll
-            for (int b = 0; b < 8; ++b) v[b] = (c0 + b > k) ? lc[c0 + b] * rl : 0.0;   // X columns stay
-            const int kn = (kk + 1) % 8;                           // column k + 1 within its sub-block (unrolled: a constant)
+            for (int b = 0; b < 8; ++b) v[b] = lc[c0 + b];
+            const int kn = (kk + 1) % 8;   // column k + 1 within its sub-block (unrolled: a constant)
             const int kbn = kb + (kk == 7 ? 1 : 0);
 #pragma unroll
             for (int a = 0; a < 8; ++a) y[a][kn] = fma(-u[a], v[kn], y[a][kn]);
             if (bj == kbn) {
 #pragma unroll
-                for (int a = 0; a < 8; ++a) Lc[(k + 1) % 3][r0 + a] = y[a][kn];
+                for (int a = 0; a < 8; ++a) Lc[(k + 1) % 3][r0 + a] = r0 + a > k + 1 ? y[a][kn] : 0.0;
+                if (bi == kbn) Pv[(k + 1) % 3] = y[kn][kn];
             }
 #pragma unroll
             for (int a = 0; a < 8; ++a)
 #pragma unroll
                 for (int b = 0; b < 8; ++b)
                     if (b != kn) y[a][b] = fma(-u[a], v[b], y[a][b]);
+            if (bj == kb) {   // column k of X starts as e_k
+#pragma unroll
+                for (int a = 0; a < 8; ++a) y[a][kk] = r0 + a == k ? 1.0 : 0.0;
+            }
+            if (bi == kb) {   // row k of X is final up to the division by l_kk
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    y[kk][b] *= rl;
+                    Xr[k & 1][c0 + b] = c0 + b <= k ? y[kk][b] : 0.0;
+                }
+            }
+            if (t < n && k < n) A[t + (int64_t)k * lda] = t == k ? lkk : lc[t] * rl;   // column k of L
             rlp = rl;
             lds_barrier();
         }
