@@ -599,7 +599,7 @@ static int launch_ct(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
     const int mw = kfast ? M / BM : 0, nw = kfast ? N / BN : 0;   // whole block rows / columns
     if (mw == bmc && nw == bnc) {
         launch_part<CT, ROLE>(s, d_tasks, ntasks, one, Part{0, 0, mw, nw, true}, xcd, fl);
-    } else if ((int64_t)mw * nw * ntasks < 1024) {
+    } else if ((int64_t)mw * nw * ntasks < 512) {
         // few whole blocks: one bounds-checked launch costs less than three on the critical path
         launch_part<CT, ROLE>(s, d_tasks, ntasks, one, Part{0, 0, bmc, bnc, false}, xcd, fl);
     } else {

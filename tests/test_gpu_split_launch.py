@@ -1,6 +1,6 @@
 """GPU parity of GEMM launches that split into a whole-block part and ragged strips.
 
-A launch whose M or N is not a multiple of 128 and that holds at least 1024 whole 128 x 128 blocks
+A launch whose M or N is not a multiple of 128 and that holds at least 512 whole 128 x 128 blocks
 runs the whole blocks on the vector path and the leftover strips, bounds-checked, on the context's
 side stream.  These cases are sized so that launches split:
   * kriging (Sec. V-A, Eq. 5/6) with n_o = 2048 at tile 256: the first steps of both blocked
