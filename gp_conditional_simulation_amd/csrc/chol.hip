@@ -81,9 +81,10 @@ __global__ void k_copy_tasks(const CopyTask* tasks, int64_t chunk) {
 
 // ---------------------------------------------------------------------------------------------
 // Leaf: factor an n x n (n <= 128) FP64 block and invert its factor in one pass of one
-// workgroup of 256 threads.  The block is a 16 x 16 grid of 8 x 8 sub-blocks, thread
-// (bi, bj) = (t / 16, t % 16) holding sub-block (bi, bj) in registers; rows and columns n..127 are
-// identity padding.  Column k of the register block is the Schur complement of A while k is
+// workgroup of 512 threads (two waves per SIMD, so that one wave's LDS and pivot latencies hide
+// behind the other's arithmetic).  The block is a 16 x 32 grid of 8 x 4 sub-blocks, thread
+// (bi, bj) = (t / 32, t % 32) holding sub-block (bi, bj) in registers; rows and columns n..127
+// are identity padding.  Column k of the register block is the Schur complement of A while k is
 // ahead of the current step and becomes column k of X = L^-1 once step k has passed, so the
 // factor and its inverse share one set of registers.
 // Column k of the Schur complement is published before step k with its pivot a_kk in a slot of
@@ -91,17 +92,19 @@ __global__ void k_copy_tasks(const CopyTask* tasks, int64_t chunk) {
 // barrier, which orders LDS only):
 //   * X update of column k - 1 (right-looking on L X = I): X_ij -= l_i,k-1 X_k-1,j, i > k - 1.
 //   * Pivot: 1 / l_kk from the hardware reciprocal square root and two Newton steps.
-//   * Schur update a_ij -= (a_ik / a_kk) a_jk for i, j > k; the owners of column k + 1 update it
-//     first and publish it.
+//   * Schur update a_ij -= (a_ik / a_kk) a_jk for i, j > k; column k + 1 is updated first and
+//     published by its owners.
 //   * Owners of column k reset it to e_k (its X part); owners of row k scale X_k,j (j <= k) by
 //     1 / l_kk and publish the row; threads 0..127 store column k of L = a_ik / l_kk to A.
-// LDS holds only the published columns (three in flight) and rows (two), so the kernel fits in
-// the registers and LDS one trailing-update workgroup frees and can run beside the update
-// kernel on the look-ahead stream.  Writes L (upper part zeroed) to A and L^-1 (upper part
-// zeroed) to T.  A non-positive pivot at local column k records col0 + k + 1 in
-// flags[FLAG_INFO] unless an earlier failure is recorded.
+// LDS holds only the published columns (three in flight) and rows (two), and the registers are
+// capped at 128 per thread, so the kernel fits in the registers and LDS one trailing-update
+// workgroup frees and can run beside the update kernel on the look-ahead stream.  Writes L
+// (upper part zeroed) to A and L^-1 (upper part zeroed) to T.  A non-positive pivot at local
+// column k records col0 + k + 1 in flags[FLAG_INFO] unless an earlier failure is recorded.
 constexpr int LEAF = 128;
-constexpr int LEAF_THREADS = 256;
+constexpr int LEAF_BR = 8, LEAF_BC = 4;                          // sub-block rows x columns
+constexpr int LEAF_GC = LEAF / LEAF_BC;                          // sub-block columns
+constexpr int LEAF_THREADS = (LEAF / LEAF_BR) * LEAF_GC;         // 512
 
 // Workgroup barrier that orders LDS accesses only.  The leaf's global stores of L need no
 // ordering against the other threads, and a full barrier would wait for them at every column.
@@ -111,47 +114,48 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__global__ __launch_bounds__(LEAF_THREADS) void k_potrf_leaf(double* A, int64_t lda, double* T, int64_t ldt,
-                                                             int n, int64_t col0, unsigned long long* flags) {
+__global__ __launch_bounds__(LEAF_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void k_potrf_leaf(double* A, int64_t lda, double* T, int64_t ldt, int n, int64_t col0, unsigned long long* flags) {
     __shared__ __attribute__((aligned(16))) double Lc[3][LEAF];   // a_ik below the diagonal, column k in slot k % 3
     __shared__ double Pv[3];                                      // a_kk in slot k % 3
     __shared__ __attribute__((aligned(16))) double Xr[2][LEAF];   // row k of X (zero beyond k) in slot k % 2
-    const int t = threadIdx.x, bi = t / 16, bj = t % 16;
-    const int r0 = bi * 8, c0 = bj * 8;
-    double y[8][8];
+    const int t = threadIdx.x, bi = t / LEAF_GC, bj = t % LEAF_GC;
+    const int r0 = bi * LEAF_BR, c0 = bj * LEAF_BC;
+    double y[LEAF_BR][LEAF_BC];
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < LEAF_BR; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < LEAF_BC; ++b) {
             const int i = r0 + a, j = c0 + b;
             y[a][b] = (j <= i && i < n) ? A[i + (int64_t)j * lda] : (i == j ? 1.0 : 0.0);
         }
     if (bj == 0) {
 #pragma unroll
-        for (int a = 0; a < 8; ++a) Lc[0][r0 + a] = r0 + a > 0 ? y[a][0] : 0.0;
+        for (int a = 0; a < LEAF_BR; ++a) Lc[0][r0 + a] = r0 + a > 0 ? y[a][0] : 0.0;
         if (bi == 0) Pv[0] = y[0][0];
     }
     __syncthreads();
-    const int nkb = (n + 7) / 8;
-    double rlp = 0.0;   // 1 / l_k-1,k-1
+    const int nkg = (n + 7) / 8;   // groups of 8 columns: one sub-block row, two sub-block columns
+    double rlp = 0.0;              // 1 / l_k-1,k-1
     int bad = 0;
-    for (int kb = 0; kb < nkb && !bad; ++kb) {
+    for (int kg = 0; kg < nkg && !bad; ++kg) {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-            const int k = kb * 8 + kk;
+            const int k = kg * 8 + kk;
+            const int cb = kg * 2 + kk / LEAF_BC, cc = kk % LEAF_BC;   // sub-block column of k, local column
             const double* lc = Lc[k % 3];
             if (k > 0) {   // X update of column k - 1: independent of this step's pivot
                 const double* lp = Lc[(k + 2) % 3];
                 const double* xp = Xr[(k + 1) & 1];
-                double u[8], v[8];
+                double u[LEAF_BR], v[LEAF_BC];
 #pragma unroll
-                for (int a = 0; a < 8; ++a) u[a] = lp[r0 + a] * rlp;
+                for (int a = 0; a < LEAF_BR; ++a) u[a] = lp[r0 + a] * rlp;
 #pragma unroll
-                for (int b = 0; b < 8; ++b) v[b] = xp[c0 + b];
+                for (int b = 0; b < LEAF_BC; ++b) v[b] = xp[c0 + b];
 #pragma unroll
-                for (int a = 0; a < 8; ++a)
+                for (int a = 0; a < LEAF_BR; ++a)
 #pragma unroll
-                    for (int b = 0; b < 8; ++b) y[a][b] = fma(-u[a], v[b], y[a][b]);
+                    for (int b = 0; b < LEAF_BC; ++b) y[a][b] = fma(-u[a], v[b], y[a][b]);
             }
             const double akk = Pv[k % 3];   // the same value in every thread: a uniform decision
             if (!(akk > 0.0)) {
@@ -163,32 +167,32 @@ __global__ __launch_bounds__(LEAF_THREADS) void k_potrf_leaf(double* A, int64_t 
             rl = fma(0.5 * rl, fma(-akk * rl, rl, 1.0), rl);
             const double lkk = akk * rl, rk = rl * rl;
             // Schur update with column k; column k + 1 first, then published
-            double u[8], v[8];
+            double u[LEAF_BR], v[LEAF_BC];
 #pragma unroll
-            for (int a = 0; a < 8; ++a) u[a] = lc[r0 + a] * rk;
+            for (int a = 0; a < LEAF_BR; ++a) u[a] = lc[r0 + a] * rk;
 #pragma unroll
-            for (int b = 0; b < 8; ++b) v[b] = lc[c0 + b];
-            const int kn = (kk + 1) % 8;   // column k + 1 within its sub-block (unrolled: a constant)
-            const int kbn = kb + (kk == 7 ? 1 : 0);
+            for (int b = 0; b < LEAF_BC; ++b) v[b] = lc[c0 + b];
+            const int cbn = kg * 2 + (kk + 1) / LEAF_BC, ccn = (kk + 1) % LEAF_BC;   // column k + 1
+            const int rbn = kg + (kk == 7 ? 1 : 0), ran = (kk + 1) % 8;              // row k + 1
 #pragma unroll
-            for (int a = 0; a < 8; ++a) y[a][kn] = fma(-u[a], v[kn], y[a][kn]);
-            if (bj == kbn) {
+            for (int a = 0; a < LEAF_BR; ++a) y[a][ccn] = fma(-u[a], v[ccn], y[a][ccn]);
+            if (bj == cbn) {
 #pragma unroll
-                for (int a = 0; a < 8; ++a) Lc[(k + 1) % 3][r0 + a] = r0 + a > k + 1 ? y[a][kn] : 0.0;
-                if (bi == kbn) Pv[(k + 1) % 3] = y[kn][kn];
+                for (int a = 0; a < LEAF_BR; ++a) Lc[(k + 1) % 3][r0 + a] = r0 + a > k + 1 ? y[a][ccn] : 0.0;
+                if (bi == rbn) Pv[(k + 1) % 3] = y[ran][ccn];
             }
 #pragma unroll
-            for (int a = 0; a < 8; ++a)
+            for (int a = 0; a < LEAF_BR; ++a)
 #pragma unroll
-                for (int b = 0; b < 8; ++b)
-                    if (b != kn) y[a][b] = fma(-u[a], v[b], y[a][b]);
-            if (bj == kb) {   // column k of X starts as e_k
+                for (int b = 0; b < LEAF_BC; ++b)
+                    if (b != ccn) y[a][b] = fma(-u[a], v[b], y[a][b]);
+            if (bj == cb) {   // column k of X starts as e_k
 #pragma unroll
-                for (int a = 0; a < 8; ++a) y[a][kk] = r0 + a == k ? 1.0 : 0.0;
+                for (int a = 0; a < LEAF_BR; ++a) y[a][cc] = r0 + a == k ? 1.0 : 0.0;
             }
-            if (bi == kb) {   // row k of X is final up to the division by l_kk
+            if (bi == kg) {   // row k of X is final up to the division by l_kk
 #pragma unroll
-                for (int b = 0; b < 8; ++b) {
+                for (int b = 0; b < LEAF_BC; ++b) {
                     y[kk][b] *= rl;
                     Xr[k & 1][c0 + b] = c0 + b <= k ? y[kk][b] : 0.0;
                 }
@@ -203,9 +207,9 @@ __global__ __launch_bounds__(LEAF_THREADS) void k_potrf_leaf(double* A, int64_t 
         return;
     }
 #pragma unroll
-    for (int a = 0; a < 8; ++a)
+    for (int a = 0; a < LEAF_BR; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
+        for (int b = 0; b < LEAF_BC; ++b) {
             const int i = r0 + a, j = c0 + b;
             if (i < n && j < n) T[i + (int64_t)j * ldt] = j <= i ? y[a][b] : 0.0;
         }
