@@ -101,8 +101,13 @@ typedef struct {
 
 /* ---- context ------------------------------------------------------------------------------ */
 /* Binds HIP device `device` and the stream `hip_stream` (a hipStream_t; NULL = null stream).
- * *out receives the context.  Errors: GPEX_ERR_ARG, GPEX_ERR_HIP. */
+ * *out receives the context.  Every entry point queues its work on that stream and, where it
+ * forks work onto streams of its own (the factorization's look-ahead stream, the context's side
+ * stream for the ragged edges of large GEMM launches, created on first use, default priority),
+ * joins them back to it with events before returning.  Errors: GPEX_ERR_ARG, GPEX_ERR_HIP. */
 int gpex_ctx_create(int device, void* hip_stream, gpex_ctx_t* out);
+/* Synchronises the context's streams and releases everything the context owns (flags, the
+ * simulation workspace, the side stream and its events).  Errors: GPEX_ERR_ARG. */
 int gpex_ctx_destroy(gpex_ctx_t ctx);
 /* Text of the last non-OK status on this context (valid until the next call on it). */
 const char* gpex_last_error(gpex_ctx_t ctx);
