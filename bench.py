@@ -17,6 +17,7 @@ block of the same workload.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--trmm-sweep | --krige]
 """
 import argparse
+import dataclasses
 import json
 import os
 import statistics
@@ -187,6 +188,8 @@ def krige_bench(args):
     import gpex_synth as syn
 
     w = syn.workload("krige20k")
+    if args.nb:
+        w = dataclasses.replace(w, nb=args.nb)
     x, y = w.locations()
     n_p, n_o = w.n_pred, w.n_obs
     dev = torch.device("cuda:0")
@@ -250,6 +253,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="unif100k_tol1e-8")
+    ap.add_argument("--nb", type=int, default=0, help="tile size override for --workload / --krige (0: the recipe's)")
     ap.add_argument("--cpu-rows", type=int, default=10240)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -279,6 +283,8 @@ def main():
     import gpex_synth as syn
 
     w = syn.workload(args.workload)
+    if args.nb:
+        w = dataclasses.replace(w, nb=args.nb)
     if w.n_obs:
         raise SystemExit("the benchmark workload is an unconditional one")
     x, y = w.locations()
