@@ -392,6 +392,11 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
             g.alpha = 1.0; g.beta = 1.0;
             od.push_back(g);
         }
+        // Task t of a batched launch runs on XCD t mod 8.  Reversing every second group of eight
+        // (a snake order) gives each XCD a near-equal share of the K = i nb work; in plain order
+        // XCD 0 gets the longest row of every group (15% above the mean at 98 tile rows).
+        for (size_t g0 = 8; g0 < od.size(); g0 += 16)
+            std::reverse(od.begin() + (std::ptrdiff_t)g0, od.begin() + (std::ptrdiff_t)std::min(g0 + 8, od.size()));
         GemmTask* d2 = nullptr;
         r = dev_alloc(ctx, (void**)&d2, sizeof(GemmTask) * (dg.size() + od.size()), "trmm panel tasks");
         if (r >= 0 && hipMemcpy(d2, dg.data(), sizeof(GemmTask) * dg.size(), hipMemcpyHostToDevice) != hipSuccess)
