@@ -511,6 +511,18 @@ static int try_typed(hipStream_t s, const GemmTask* d_tasks, int ntasks, const G
             return 1;
         }
     }
+    if constexpr (sizeof(CT) == 4 && ROLE == GEMM_TRMM && TRA == 0 && TRB == 0 && sizeof(TA) == 8) {
+        // diagonal tiles of the simulation product: 2 x 4 waves (128 x 256 blocks) read each FP64
+        // tile half as often as 128 x 128 blocks
+        const bool whole = p.m_off == 0 && p.n_off == 0 && p.bmc * 128 == one.M && p.bnc * 128 == one.N;
+        if (whole && one.N % 256 == 0) {
+            const Part w{0, 0, one.M / 128, one.N / 256, true};
+            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 4, 4, 1>),
+                               dim3((unsigned)part_grid(w, ntasks, xcd)), dim3(512), 0, s, d_tasks, one, ntasks, w.bmc,
+                               w.bnc, 0, 0, xcd, fl);
+            return 1;
+        }
+    }
     hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 2, 4, 1>), dim3(grid), dim3(NTHR), 0, s,
                        d_tasks, one, ntasks, p.bmc, p.bnc, p.m_off, p.n_off, xcd, fl);
     return 1;
