@@ -230,10 +230,15 @@ __global__ void k_join(const double* ws, double* A, int64_t lda, double* T, int6
     }
 }
 
+// Size of the first half when a diagonal block of order n > LEAF is split: whole leaves first
+// (a multiple of LEAF, half of ceil(n / LEAF) leaves), so the recursion ends in the fewest leaves
+// ceil(n / LEAF) and the fewest halving steps; orders that are multiples of 2 LEAF halve exactly.
+static int split_first(int n) { return LEAF * (((n + LEAF - 1) / LEAF) / 2); }
+
 // Footprint in doubles of the workspace potrf_inv uses for order n: n^2 / 2 (rounded up).
 static int64_t potrf_ws_need(int n) {
     if (n <= LEAF) return 0;
-    const int n1 = ((n / 2 + 15) / 16) * 16, n2 = n - n1;
+    const int n1 = split_first(n), n2 = n - n1;
     const int64_t blk = (int64_t)n2 * n1;
     return std::max(blk, potrf_ws_need(n2)) + blk;
 }
@@ -254,7 +259,7 @@ int potrf_inv(gpex_ctx_t ctx, hipStream_t s, double* A, int64_t lda, double* T, 
         GPEX_HIP(ctx, hipGetLastError());
         return GPEX_OK;
     }
-    const int n1 = ((n / 2 + 15) / 16) * 16, n2 = n - n1;
+    const int n1 = split_first(n), n2 = n - n1;
     double* A21 = A + n1;
     double* A22 = A + n1 + (int64_t)n1 * lda;
     double* T21 = T + n1;
