@@ -26,8 +26,10 @@ OK, ERR_ARG, ERR_HIP, ERR_NOMEM, ERR_STATE = 0, -1, -2, -3, -4
 ERR_NOT_SPD, ERR_MSPE_NONPOS, ERR_EMPTY_SAMPLE, WARN_CHECKS_FAILED, WARN_FP16_OVERFLOW = 1, 2, 3, 4, 5
 STATUS_NAMES = {0: "OK", -1: "ERR_ARG", -2: "ERR_HIP", -3: "ERR_NOMEM", -4: "ERR_STATE", 1: "ERR_NOT_SPD",
                 2: "ERR_MSPE_NONPOS", 3: "ERR_EMPTY_SAMPLE", 4: "WARN_CHECKS_FAILED", 5: "WARN_FP16_OVERFLOW"}
-EXPORTS = ["gpex_version", "gpex_ctx_create", "gpex_ctx_destroy", "gpex_last_error", "gpex_cov_gen",
-           "gpex_tiled_info", "gpex_tiled_stats", "gpex_tiled_to_dense", "gpex_tiled_block", "gpex_tiled_destroy",
+EXPORTS = ["gpex_version", "gpex_ctx_create", "gpex_ctx_destroy", "gpex_ctx_release_workspace", "gpex_ctx_set_serial",
+           "gpex_last_error", "gpex_cov_gen",
+           "gpex_tiled_info", "gpex_tiled_stats", "gpex_tiled_to_dense", "gpex_tiled_block", "gpex_tiled_block_raw",
+           "gpex_tiled_destroy",
            "gpex_potrf_mp", "gpex_normals", "gpex_trmm_sim", "gpex_krige", "gpex_excursion_regions",
            "gpex_plan", "gpex_ctx_set_timing", "gpex_ctx_timings"]
 
@@ -39,7 +41,7 @@ class CovParams(C.Structure):
 
 class PrecOpts(C.Structure):
     _fields_ = [("amp", C.c_int), ("tol", C.c_double), ("allow_fp16", C.c_int), ("unscaled_rule", C.c_int),
-                ("auto_tol", C.c_int)]
+                ("auto_tol", C.c_int), ("fp16_dest_emulation", C.c_int)]
 
 
 class Diag(C.Structure):
@@ -47,7 +49,7 @@ class Diag(C.Structure):
                 ("l_bound_sub", C.c_double), ("r_hp", C.c_double), ("rho1", C.c_double), ("rho2", C.c_double),
                 ("norm_B", C.c_double), ("eq10_pass", C.c_int), ("eq11_pass", C.c_int),
                 ("lower_exceeds_upper", C.c_int), ("fp16_overflow", C.c_int), ("tiles", C.c_int64 * 3),
-                ("tol", C.c_double), ("tol_reductions", C.c_int64)]
+                ("tol", C.c_double), ("tol_reductions", C.c_int64), ("u_factor", C.c_double)]
 
     def to_dict(self) -> dict:
         d = {k: getattr(self, k) for k, _ in self._fields_ if k != "tiles"}
@@ -57,6 +59,11 @@ class Diag(C.Structure):
 
 class RegionStats(C.Structure):
     _fields_ = [("q_in", C.c_double), ("q_out", C.c_double), ("n_psi", C.c_int64), ("n_phi", C.c_int64)]
+
+
+# Device allocator callbacks handed to gpex_ctx_create: void* alloc(size_t, void*), void free(void*, void*).
+_ALLOC_FN = C.CFUNCTYPE(C.c_void_p, C.c_size_t, C.c_void_p)
+_FREE_FN = C.CFUNCTYPE(None, C.c_void_p, C.c_void_p)
 
 
 class GpexError(RuntimeError):
@@ -80,14 +87,17 @@ def lib():
         L.gpex_version.restype = C.c_char_p
         L.gpex_last_error.restype = C.c_char_p
         L.gpex_last_error.argtypes = [P]
-        L.gpex_ctx_create.argtypes = [I, P, C.POINTER(P)]
+        L.gpex_ctx_create.argtypes = [I, P, _ALLOC_FN, _FREE_FN, P, C.POINTER(P)]
         L.gpex_ctx_destroy.argtypes = [P]
+        L.gpex_ctx_release_workspace.argtypes = [P]
+        L.gpex_ctx_set_serial.argtypes = [P, I]
         L.gpex_cov_gen.argtypes = [P, P, I64, P, C.POINTER(CovParams), I, C.POINTER(PrecOpts), C.POINTER(P),
                                    C.POINTER(Diag)]
         L.gpex_tiled_info.argtypes = [P, C.POINTER(I64), C.POINTER(I), C.POINTER(I64), P, C.POINTER(D)]
         L.gpex_tiled_stats.argtypes = [P, P]
         L.gpex_tiled_to_dense.argtypes = [P, P, P, I64]
         L.gpex_tiled_block.argtypes = [P, P, I64, I64, I64, I64, P, I64]
+        L.gpex_tiled_block_raw.argtypes = [P, P, I, I64, I64, I64, I64, P, I64]
         L.gpex_tiled_destroy.argtypes = [P]
         L.gpex_potrf_mp.argtypes = [P, P, C.POINTER(I64)]
         L.gpex_normals.argtypes = [P, U64, C.c_uint32, I64, I64, P, I64]
@@ -134,14 +144,31 @@ def _dev_check(t, ctx, dtype=None):
 
 
 class Context:
-    """A library context bound to one device and one torch stream (default: the current one)."""
+    """A library context bound to one device and one torch stream (default: the current one).
 
-    def __init__(self, device: int = 0, stream=None):
+    The library's device memory (tile storage, workspaces) comes from torch's caching allocator on
+    that stream, so repeated runs reuse cached blocks instead of calling hipMalloc / hipFree."""
+
+    def __init__(self, device: int = 0, stream=None, torch_alloc: bool = True):
         import torch
         self.device = device
         self.stream = stream if stream is not None else torch.cuda.current_stream(device)
+        sp = self.stream.cuda_stream
+
+        def _alloc(nbytes, _user):
+            try:
+                return torch.cuda.caching_allocator_alloc(int(nbytes), device, sp)
+            except Exception:   # out of memory: the library reports GPEX_ERR_NOMEM
+                return None
+
+        def _free(ptr, _user):
+            torch.cuda.caching_allocator_delete(ptr)
+
+        # the callbacks must live as long as anything allocated through them
+        self._alloc = _ALLOC_FN(_alloc) if torch_alloc else _ALLOC_FN()
+        self._free = _FREE_FN(_free) if torch_alloc else _FREE_FN()
         h = C.c_void_p()
-        rc = lib().gpex_ctx_create(device, C.c_void_p(self.stream.cuda_stream), C.byref(h))
+        rc = lib().gpex_ctx_create(device, C.c_void_p(sp), self._alloc, self._free, None, C.byref(h))
         if rc != 0:
             raise GpexError(rc, "gpex_ctx_create failed")
         self.h = h
@@ -165,15 +192,24 @@ class Context:
     def set_timing(self, on: bool):
         self.check(lib().gpex_ctx_set_timing(self.h, int(on)))
 
+    def set_serial(self, on: bool):
+        """Serial schedule: every launch on the context stream (bitwise the same results)."""
+        self.check(lib().gpex_ctx_set_serial(self.h, int(on)))
+
+    def release_workspace(self):
+        self.check(lib().gpex_ctx_release_workspace(self.h))
+
     def timings(self) -> dict:
-        out = (C.c_double * 16)()
+        out = (C.c_double * 32)()
         self.check(lib().gpex_ctx_timings(self.h, out))
         v = list(out)
         return {"potrf_ms": v[0],
                 "update_ms": {"fp64": v[1], "fp32": v[4], "fp16": v[7]},
                 "update_launches": {"fp64": int(v[2]), "fp32": int(v[5]), "fp16": int(v[8])},
                 "update_flops": {"fp64": v[3], "fp32": v[6], "fp16": v[9]},
-                "trmm_ms": v[10], "trmm_kernels_ms": v[11]}
+                "update_flops_exact": {"fp64": v[12], "fp32": v[13], "fp16": v[14]},
+                "update_busy_ms": {"fp64": v[15], "fp32": v[16], "fp16": v[17]},
+                "trmm_ms": v[10], "trmm_kernels_ms": v[11], "trmm_rows_ms": v[18]}
 
 
 @dataclasses.dataclass
@@ -183,6 +219,7 @@ class Tiled:
     h: C.c_void_p
     diag: dict
     status: int
+    potrf_status: int = 0
 
     def info(self) -> dict:
         n, nb, nt, s = C.c_int64(), C.c_int(), C.c_int64(), C.c_double()
@@ -212,6 +249,13 @@ class Tiled:
         self.ctx.check(lib().gpex_tiled_block(self.ctx.h, self.h, r0, c0, rows, cols, _cm(out), rows))
         return out
 
+    def block_raw(self, r0: int, c0: int, rows: int, cols: int, fp16_copy: bool = False):
+        """Stored values (or the FP16 copy of the factor) of a block, exactly, without unscaling."""
+        out = colmajor(rows, cols, self.ctx)
+        self.ctx.check(lib().gpex_tiled_block_raw(self.ctx.h, self.h, int(fp16_copy), r0, c0, rows, cols, _cm(out),
+                                                  rows))
+        return out
+
     def close(self):
         if self.h:
             lib().gpex_tiled_destroy(self.h)
@@ -225,14 +269,15 @@ class Tiled:
 
 
 def cov_gen(ctx: Context, loc, n: int, params: dict, nb: int, amp: int = 0, tol: float = 0.0,
-            allow_fp16: bool = True, nt_rule: bool = True, diag_add=None, auto_tol: bool = False) -> Tiled:
+            allow_fp16: bool = True, nt_rule: bool = True, diag_add=None, auto_tol: bool = False,
+            fp16_dest: bool = False) -> Tiled:
     """gpex_cov_gen.  loc: float64 device tensor of 2n values (x then y)."""
     import torch
     _dev_check(loc, ctx, torch.float64)
     _dev_check(diag_add, ctx, torch.float64)
     cp = CovParams(int(params.get("kind", 0)), float(params["sigma2"]), float(params["range"]),
                    float(params.get("nu", 0.5)), float(params.get("nugget", 0.0)))
-    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(not nt_rule), int(auto_tol))
+    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(not nt_rule), int(auto_tol), int(fp16_dest))
     h = C.c_void_p()
     d = Diag()
     rc = lib().gpex_cov_gen(ctx.h, _ptr(loc), n, _ptr(diag_add), C.byref(cp), nb, C.byref(po), C.byref(h),
@@ -242,12 +287,16 @@ def cov_gen(ctx: Context, loc, n: int, params: dict, nb: int, amp: int = 0, tol:
 
 
 def potrf_mp(ctx: Context, a: Tiled) -> int:
-    """gpex_potrf_mp; returns info (0 or the failing column); raises on error."""
+    """gpex_potrf_mp; returns info (0 or the failing column); raises on error.  The status
+    (OK or WARN_FP16_OVERFLOW) is kept in a.potrf_status."""
     info = C.c_int64()
     rc = lib().gpex_potrf_mp(ctx.h, a.h, C.byref(info))
+    a.potrf_status = rc
     if rc == ERR_NOT_SPD:
         return info.value
-    ctx.check(rc)
+    ctx.check(rc, allow=(OK, WARN_FP16_OVERFLOW))
+    if rc == WARN_FP16_OVERFLOW:
+        a.diag["fp16_overflow"] = 1
     return info.value
 
 
@@ -266,7 +315,7 @@ def plan(stats, nt: int, amp: int = 1, tol: float = 0.0, allow_fp16: bool = True
     if st.size != 3 * nt * (nt + 1) // 2:
         raise ValueError("stats must hold 3 values per lower tile")
     pmap = np.zeros((nt, nt), dtype=np.uint8)
-    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(not nt_rule), int(auto_tol))
+    po = PrecOpts(int(amp), float(tol), int(allow_fp16), int(not nt_rule), int(auto_tol), 0)
     d = Diag()
     rc = lib().gpex_plan(st.ctypes.data, nt, C.byref(po), pmap.ctypes.data, C.byref(d))
     if rc != 0:
@@ -280,9 +329,10 @@ def colmajor(rows: int, cols: int, ctx: "Context", dtype=None):
     return torch.empty((cols, rows), dtype=dtype or torch.float64, device=f"cuda:{ctx.device}").T
 
 
-def trmm_sim(ctx: Context, L: Tiled, nsim: int, seed: int = 0, Z=None, M=None, want_diag=True):
+def trmm_sim(ctx: Context, L: Tiled, nsim: int, seed: int = 0, Z=None, M=None, want_diag=True, status=False):
     """gpex_trmm_sim.  Z: explicit normals, column-major n x nsim view (or None: seeded normals).
-    Returns (M as a column-major n x nsim view, diag dict or None)."""
+    Returns (M as a column-major n x nsim view, diag dict or None), plus the status code (OK or
+    WARN_FP16_OVERFLOW) when status=True."""
     import torch
     n = L.info()["n"]
     if M is None:
@@ -291,8 +341,9 @@ def trmm_sim(ctx: Context, L: Tiled, nsim: int, seed: int = 0, Z=None, M=None, w
     _dev_check(M, ctx, torch.float64)
     d = Diag()
     rc = lib().gpex_trmm_sim(ctx.h, L.h, nsim, seed, _cm(Z), _cm(M), n, C.byref(d) if want_diag else None)
-    ctx.check(rc)
-    return M, (d.to_dict() if want_diag else None)
+    ctx.check(rc, allow=(OK, WARN_FP16_OVERFLOW))
+    out = (M, (d.to_dict() if want_diag else None))
+    return out + (rc,) if status else out
 
 
 def krige(ctx: Context, loc_o, n_o: int, loc_p, n_p: int, y_o, k_trend: int, params: dict, tau2: float,

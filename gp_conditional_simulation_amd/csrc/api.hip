@@ -10,21 +10,67 @@ int set_err(gpex_ctx_t ctx, int code, const std::string& msg) {
     return code;
 }
 
-int dev_alloc(gpex_ctx_t ctx, void** p, size_t bytes, const char* what) {
-    *p = nullptr;
-    if (bytes == 0) bytes = 256;
-    hipError_t e = hipMalloc(p, bytes);
-    if (e != hipSuccess) {
+static void* raw_alloc(void* (*alloc)(size_t, void*), void* user, size_t bytes) {
+    if (alloc) return alloc(bytes, user);
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
         (void)hipGetLastError();
-        *p = nullptr;
-        return set_err(ctx, GPEX_ERR_NOMEM,
-                       std::string("device allocation failed (") + what + ", " + std::to_string(bytes) + " bytes)");
+        return nullptr;
     }
+    return p;
+}
+
+static void raw_free(void (*dealloc)(void*, void*), void* user, void* p) {
+    if (!p) return;
+    if (dealloc) dealloc(p, user);
+    else (void)hipFree(p);
+}
+
+static int nomem(gpex_ctx_t ctx, const char* what, size_t bytes) {
+    return set_err(ctx, GPEX_ERR_NOMEM,
+                   std::string("device allocation failed (") + what + ", " + std::to_string(bytes) + " bytes)");
+}
+
+int dev_alloc(gpex_ctx_t ctx, void** p, size_t bytes, const char* what) {
+    if (bytes == 0) bytes = 256;
+    *p = raw_alloc(ctx->alloc, ctx->user, bytes);
+    return *p ? GPEX_OK : nomem(ctx, what, bytes);
+}
+
+void dev_free(gpex_ctx_t ctx, void* p) { raw_free(ctx->dealloc, ctx->user, p); }
+
+int tiled_alloc(gpex_ctx_t ctx, gpex_tiled_t t, void** p, size_t bytes, const char* what) {
+    if (bytes == 0) bytes = 256;
+    *p = raw_alloc(t->alloc, t->user, bytes);
+    return *p ? GPEX_OK : nomem(ctx, what, bytes);
+}
+
+void tiled_free(gpex_tiled_t t, void* p) { raw_free(t->dealloc, t->user, p); }
+
+int ws_get(gpex_ctx_t ctx, int slot, size_t bytes, void** out, const char* what) {
+    auto& w = ctx->ws[slot];
+    if (w.bytes < bytes) {
+        // the old buffer's last users are ordered before this point on the context stream: a
+        // stream-ordered allocator may hand it out again, hipFree waits for the device
+        dev_free(ctx, w.p);
+        w.p = nullptr;
+        w.bytes = 0;
+        const size_t grown = (bytes + (2u << 20) - 1) / (2u << 20) * (2u << 20);   // 2 MiB granules
+        GPEX_TRY(dev_alloc(ctx, &w.p, grown, what));
+        w.bytes = grown;
+    }
+    *out = w.p;
     return GPEX_OK;
 }
 
-void dev_free(void* p) {
-    if (p) (void)hipFree(p);
+int ctx_event(gpex_ctx_t ctx, size_t i, hipEvent_t* out) {
+    while (ctx->events.size() <= i) {
+        hipEvent_t e;
+        GPEX_HIP(ctx, hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        ctx->events.push_back(e);
+    }
+    *out = ctx->events[i];
+    return GPEX_OK;
 }
 
 }  // namespace gpex
@@ -33,21 +79,27 @@ using namespace gpex;
 
 extern "C" const char* gpex_version(void) { return "gpex 0.1 (gfx950)"; }
 
-extern "C" int gpex_ctx_create(int device, void* hip_stream, gpex_ctx_t* out) {
+extern "C" int gpex_ctx_create(int device, void* hip_stream, void* (*alloc)(size_t, void*),
+                               void (*dealloc)(void*, void*), void* user, gpex_ctx_t* out) {
     if (!out) return GPEX_ERR_ARG;
     *out = nullptr;
+    if ((alloc == nullptr) != (dealloc == nullptr)) return GPEX_ERR_ARG;
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return GPEX_ERR_ARG;
     if (hipSetDevice(device) != hipSuccess) return GPEX_ERR_HIP;
     auto* c = new gpex_ctx_s();
     c->device = device;
     c->stream = static_cast<hipStream_t>(hip_stream);
-    if (hipMalloc(&c->d_flags, sizeof(long long) * FLAG_COUNT) != hipSuccess) {
+    c->alloc = alloc;
+    c->dealloc = dealloc;
+    c->user = user;
+    if (dev_alloc(c, (void**)&c->d_flags, sizeof(long long) * FLAG_COUNT, "flags") != GPEX_OK) {
         delete c;
         return GPEX_ERR_NOMEM;
     }
-    if (hipMemset(c->d_flags, 0, sizeof(long long) * FLAG_COUNT) != hipSuccess) {
-        (void)hipFree(c->d_flags);
+    if (hipMemsetAsync(c->d_flags, 0, sizeof(long long) * FLAG_COUNT, c->stream) != hipSuccess ||
+        hipStreamSynchronize(c->stream) != hipSuccess) {
+        dev_free(c, c->d_flags);
         delete c;
         return GPEX_ERR_HIP;
     }
@@ -55,20 +107,42 @@ extern "C" int gpex_ctx_create(int device, void* hip_stream, gpex_ctx_t* out) {
     return GPEX_OK;
 }
 
+static void release_workspace(gpex_ctx_t ctx) {
+    for (auto& w : ctx->ws) {
+        dev_free(ctx, w.p);
+        w.p = nullptr;
+        w.bytes = 0;
+    }
+}
+
+extern "C" int gpex_ctx_release_workspace(gpex_ctx_t ctx) {
+    if (!ctx) return GPEX_ERR_ARG;
+    GPEX_HIP(ctx, hipSetDevice(ctx->device));
+    GPEX_HIP(ctx, hipStreamSynchronize(ctx->stream));
+    release_workspace(ctx);
+    return GPEX_OK;
+}
+
 extern "C" int gpex_ctx_destroy(gpex_ctx_t ctx) {
     if (!ctx) return GPEX_ERR_ARG;
     (void)hipSetDevice(ctx->device);
-    if (ctx->stream) (void)hipStreamSynchronize(ctx->stream);
-    else (void)hipDeviceSynchronize();
-    dev_free(ctx->d_flags);
-    dev_free(ctx->sim_ws);
-    if (ctx->side) {
-        (void)hipStreamSynchronize(ctx->side);
-        (void)hipStreamDestroy(ctx->side);
-    }
+    (void)hipStreamSynchronize(ctx->stream);
+    if (ctx->side) (void)hipStreamSynchronize(ctx->side);
+    if (ctx->ahead) (void)hipStreamSynchronize(ctx->ahead);
+    release_workspace(ctx);
+    dev_free(ctx, ctx->d_flags);
+    if (ctx->side) (void)hipStreamDestroy(ctx->side);
+    if (ctx->ahead) (void)hipStreamDestroy(ctx->ahead);
     if (ctx->side_fork) (void)hipEventDestroy(ctx->side_fork);
     if (ctx->side_join) (void)hipEventDestroy(ctx->side_join);
+    for (auto e : ctx->events) (void)hipEventDestroy(e);
     delete ctx;
+    return GPEX_OK;
+}
+
+extern "C" int gpex_ctx_set_serial(gpex_ctx_t ctx, int on) {
+    if (!ctx) return GPEX_ERR_ARG;
+    ctx->serial = on != 0;
     return GPEX_OK;
 }
 
@@ -82,7 +156,7 @@ extern "C" int gpex_ctx_set_timing(gpex_ctx_t ctx, int on) {
 
 extern "C" int gpex_ctx_timings(gpex_ctx_t ctx, double* out) {
     if (!ctx || !out) return GPEX_ERR_ARG;
-    for (int i = 0; i < 16; ++i) out[i] = ctx->timings[i];
+    for (int i = 0; i < 32; ++i) out[i] = ctx->timings[i];
     return GPEX_OK;
 }
 
@@ -117,10 +191,11 @@ extern "C" int gpex_tiled_stats(gpex_tiled_t t, double* h_stats) {
 extern "C" int gpex_tiled_destroy(gpex_tiled_t t) {
     if (!t) return GPEX_ERR_ARG;
     (void)hipSetDevice(t->device);
-    (void)hipDeviceSynchronize();
-    dev_free(t->base);
-    dev_free(t->tinv);
-    dev_free(t->l16);
+    // a stream-ordered allocator orders the reuse after the queued work on the context stream;
+    // hipFree waits for the device by itself
+    tiled_free(t, t->base);
+    tiled_free(t, t->tinv);
+    tiled_free(t, t->l16);
     delete t;
     return GPEX_OK;
 }

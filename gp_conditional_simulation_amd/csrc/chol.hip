@@ -316,25 +316,21 @@ using namespace gpex;
 extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     if (!ctx) return GPEX_ERR_ARG;
     if (!a || !info) return set_err(ctx, GPEX_ERR_ARG, "gpex_potrf_mp: null handle or info");
+    if (a->failed) return set_err(ctx, GPEX_ERR_STATE, "gpex_potrf_mp: an earlier factorization of this matrix failed");
     if (a->factored) return set_err(ctx, GPEX_ERR_STATE, "gpex_potrf_mp: matrix already factored");
     GPEX_HIP(ctx, hipSetDevice(ctx->device));
     const int64_t nt = a->nt;
     const int nb = a->nb;
     const size_t tile_el = (size_t)nb * nb;
     hipStream_t s = ctx->stream;
-    if (!a->tinv) GPEX_TRY(dev_alloc(ctx, (void**)&a->tinv, sizeof(double) * tile_el * nt, "inverse diagonal tiles"));
+    if (!a->tinv)
+        GPEX_TRY(tiled_alloc(ctx, a, (void**)&a->tinv, sizeof(double) * tile_el * nt, "inverse diagonal tiles"));
     // FP16 copy of the off-diagonal factor for the simulation product, written by the panel solves
     if (a->opts.amp && nt > 1 && !a->l16)
-        GPEX_TRY(dev_alloc(ctx, (void**)&a->l16, sizeof(_Float16) * tile_el * (size_t)(nt * (nt - 1) / 2),
-                           "FP16 factor panels"));
-    void* pws = nullptr;
-    double* ws = nullptr;
-    if (nt > 1) GPEX_TRY(dev_alloc(ctx, &pws, 8 * tile_el * (nt - 1), "panel workspace"));
-    GPEX_TRY(dev_alloc(ctx, (void**)&ws, sizeof(double) * tile_el, "diagonal workspace"));
-    auto cleanup = [&]() {
-        dev_free(pws);
-        dev_free(ws);
-    };
+        GPEX_TRY(tiled_alloc(ctx, a, (void**)&a->l16, sizeof(_Float16) * tile_el * (size_t)(nt * (nt - 1) / 2),
+                             "FP16 factor panels"));
+    // rows of tile row i that exist (the last one may be padding beyond n)
+    auto rows = [&](int64_t i) { return (double)std::min<int64_t>(nb, a->n - i * nb); };
 
     // Per-step task groups, built once on the host and uploaded in one copy.  A group holds the
     // tasks of one step with one compute precision and one operand-type signature (a launch runs
@@ -346,14 +342,25 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     std::vector<Group> groups;
     std::vector<int64_t> group_beg((size_t)nt + 1, 0);
     std::vector<int64_t> copy_beg((size_t)nt + 1, 0);
-    std::vector<double> upd_flops(3, 0.0);
+    std::vector<double> upd_flops(3, 0.0), upd_flops_exact(3, 0.0);
     auto sig = [](int compute, const GemmTask& g) {
         return compute * 1000 + g.ta * 100 + g.tb * 10 + g.tc;
     };
+    // workspace: panel copies (FP64-sized slots), diagonal scratch, task and copy lists
+    Carve cv;
+    const size_t p_pws = cv.add(nt > 1 ? 8 * tile_el * (size_t)(nt - 1) : 0), p_ws = cv.add(sizeof(double) * tile_el);
+    size_t ntask = 0;
+    for (int64_t k = 0; k < nt; ++k) ntask += (size_t)(nt - k - 1) + (size_t)(nt - k - 1) * (nt - k) / 2;
+    const size_t p_tasks = cv.add(sizeof(GemmTask) * ntask), p_copies = cv.add(sizeof(CopyTask) * (size_t)(nt * (nt - 1) / 2));
+    void* wsb = nullptr;
+    GPEX_TRY(ws_get(ctx, WS_POTRF, cv.total, &wsb, "factorization workspace"));
+    uint8_t* pws = cv.get<uint8_t>(wsb, p_pws);
+    double* ws = cv.get<double>(wsb, p_ws);
+    GemmTask* d_tasks = cv.get<GemmTask>(wsb, p_tasks);
+    CopyTask* d_copies = cv.get<CopyTask>(wsb, p_copies);
     for (int64_t k = 0; k < nt; ++k) {
         for (int64_t i = k + 1; i < nt; ++i) {
-            CopyTask c{a->tile(i, k), static_cast<uint8_t*>(pws) + 8 * tile_el * (i - k - 1),
-                       (int64_t)(dt_size(a->prec(i, k)) * tile_el)};
+            CopyTask c{a->tile(i, k), pws + 8 * tile_el * (i - k - 1), (int64_t)(dt_size(a->prec(i, k)) * tile_el)};
             copies.push_back(c);
         }
         copy_beg[(size_t)k + 1] = (int64_t)copies.size();
@@ -362,7 +369,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         for (int64_t i = k + 1; i < nt; ++i) {
             int p = a->prec(i, k);
             GemmTask g{};
-            g.A = static_cast<uint8_t*>(pws) + 8 * tile_el * (i - k - 1);
+            g.A = pws + 8 * tile_el * (i - k - 1);
             g.B = a->tinv_tile(k);
             g.C = a->tile(i, k);
             g.lda = g.ldb = g.ldc = nb;
@@ -392,6 +399,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
                 g.tri = (i == j) ? TRI_C_LOWER : 0;   // diagonal tiles: only the lower triangle is used
                 (j == k + 1 ? update_next : update)[sig(p, g)].push_back(g);
                 upd_flops[(size_t)p] += (i == j ? 1.0 : 2.0) * nb * (double)nb * nb;
+                upd_flops_exact[(size_t)p] += (i == j ? 1.0 : 2.0) * rows(i) * rows(j) * rows(k);
             }
         for (auto& kv : panel) {
             groups.push_back(Group{(int64_t)tasks.size(), 0, DT_F64, GEMM_GENERIC, (int)k, 0});
@@ -406,31 +414,14 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             }
     }
     group_beg[(size_t)nt] = (int64_t)groups.size();
-    GemmTask* d_tasks = nullptr;
-    CopyTask* d_copies = nullptr;
-    if (!tasks.empty()) {
-        int r = dev_alloc(ctx, (void**)&d_tasks, sizeof(GemmTask) * tasks.size(), "task lists");
-        if (r < 0) { cleanup(); return r; }
-        (void)hipMemcpy(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice);
-    }
-    if (!copies.empty()) {
-        int r = dev_alloc(ctx, (void**)&d_copies, sizeof(CopyTask) * copies.size(), "copy lists");
-        if (r < 0) { cleanup(); dev_free(d_tasks); return r; }
-        (void)hipMemcpy(d_copies, copies.data(), sizeof(CopyTask) * copies.size(), hipMemcpyHostToDevice);
-    }
-    auto cleanup_all = [&]() {
-        cleanup();
-        dev_free(d_tasks);
-        dev_free(d_copies);
-    };
-#define POTRF_TRY(expr)                      \
-    do {                                     \
-        int r_ = (expr);                     \
-        if (r_ < 0) { cleanup_all(); return r_; } \
-    } while (0)
+    if (tasks.size() > ntask || copies.size() > (size_t)(nt * (nt - 1) / 2))
+        return set_err(ctx, GPEX_ERR_STATE, "gpex_potrf_mp: task count exceeds its workspace");
+    // uploads are ordered after earlier users of the workspace on the context stream; the host
+    // vectors stay alive until the final synchronisation
+    if (!tasks.empty()) GPEX_HIP(ctx, hipMemcpyAsync(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice, s));
+    if (!copies.empty()) GPEX_HIP(ctx, hipMemcpyAsync(d_copies, copies.data(), sizeof(CopyTask) * copies.size(), hipMemcpyHostToDevice, s));
+    GPEX_HIP(ctx, hipMemsetAsync(ctx->d_flags + FLAG_INFO, 0, sizeof(long long) * (FLAG_BADTASK + 1), s));
 
-    POTRF_TRY(hipMemsetAsync(ctx->d_flags + FLAG_INFO, 0, sizeof(long long) * (FLAG_BADTASK + 1), s) == hipSuccess
-                  ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "memset flags"));
     Timer tm{ctx};
     struct Rec { hipEvent_t b, e; int prec; };
     std::vector<Rec> recs;
@@ -442,40 +433,31 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     // Look-ahead of depth one on two streams (both at the default priority):
     //   stream A (the context stream): [wait rest(k-1)] next-column update of step k, then the panel
     //            work of step k+1 (diagonal factor + inverse, panel copy, panel solves);
-    //   stream B: [wait panel(k)] the rest of step k's trailing update.
+    //   stream B (the context's look-ahead stream): [wait panel(k)] the rest of step k's update.
     // The panel work of step k+1 thus overlaps the bulk update of step k.  Tiles touched
     // concurrently are disjoint: rest(k) writes columns >= k+2, the panel of k+1 column k+1.
-    hipStream_t sb = nullptr;
+    // In serial mode stream B is the context stream: the same launches in the same order per tile.
+    const bool two = !ctx->serial && nt > 1;
+    if (two && !ctx->ahead) GPEX_HIP(ctx, hipStreamCreateWithFlags(&ctx->ahead, hipStreamNonBlocking));
+    hipStream_t sb = two ? ctx->ahead : s;
+    // events: fork, then panel(k) and rest(k) per step
     hipEvent_t evfork = nullptr;
     std::vector<hipEvent_t> evp((size_t)nt, nullptr), evr((size_t)nt, nullptr);
-    auto release_sync = [&]() {
-        if (evfork) (void)hipEventDestroy(evfork);
-        for (auto e : evp) if (e) (void)hipEventDestroy(e);
-        for (auto e : evr) if (e) (void)hipEventDestroy(e);
-        if (sb) (void)hipStreamDestroy(sb);
-    };
-    if (hipStreamCreateWithFlags(&sb, hipStreamNonBlocking) != hipSuccess) {
-        cleanup_all();
-        return set_err(ctx, GPEX_ERR_HIP, "potrf: second stream");
-    }
-    if (hipEventCreateWithFlags(&evfork, hipEventDisableTiming) != hipSuccess) {
-        release_sync();
-        cleanup_all();
-        return set_err(ctx, GPEX_ERR_HIP, "potrf: events");
-    }
-    for (int64_t k = 0; k < nt; ++k) {
-        if (hipEventCreateWithFlags(&evp[(size_t)k], hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&evr[(size_t)k], hipEventDisableTiming) != hipSuccess) {
-            release_sync();
-            cleanup_all();
-            return set_err(ctx, GPEX_ERR_HIP, "potrf: events");
+    if (two) {
+        GPEX_TRY(ctx_event(ctx, 0, &evfork));
+        for (int64_t k = 0; k < nt; ++k) {
+            GPEX_TRY(ctx_event(ctx, 1 + 2 * (size_t)k, &evp[(size_t)k]));
+            GPEX_TRY(ctx_event(ctx, 2 + 2 * (size_t)k, &evr[(size_t)k]));
         }
     }
-#define POTRF_TRY2(expr)                                   \
-    do {                                                   \
-        int r2_ = (expr);                                  \
-        if (r2_ < 0) { (void)hipStreamSynchronize(sb); (void)hipStreamSynchronize(s); release_sync(); cleanup_all(); return r2_; } \
-    } while (0)
+    auto record = [&](hipEvent_t e, hipStream_t st) -> int {
+        if (two) GPEX_HIP(ctx, hipEventRecord(e, st));
+        return GPEX_OK;
+    };
+    auto wait = [&](hipStream_t st, hipEvent_t e) -> int {
+        if (two) GPEX_HIP(ctx, hipStreamWaitEvent(st, e, 0));
+        return GPEX_OK;
+    };
     auto launch_groups = [&](int64_t k, int want_role, int want_next, hipStream_t st) -> int {
         for (int64_t gi = group_beg[(size_t)k]; gi < group_beg[(size_t)k + 1]; ++gi) {
             const Group& G = groups[(size_t)gi];
@@ -486,8 +468,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
                 rc.b = tm.next();
                 (void)hipEventRecord(rc.b, st);
             }
-            int r = gemm_launch(ctx, st, G.compute, d_tasks + G.b0, (int)(G.b1 - G.b0), tasks[(size_t)G.b0], G.role);
-            if (r < 0) return r;
+            GPEX_TRY(gemm_launch(ctx, st, G.compute, d_tasks + G.b0, (int)(G.b1 - G.b0), tasks[(size_t)G.b0], G.role));
             if (ctx->timing && upd) {
                 rc.e = tm.next();
                 (void)hipEventRecord(rc.e, st);
@@ -508,33 +489,34 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         }
         return launch_groups(k, GEMM_GENERIC, 0, s);
     };
-    // fork: stream B starts after everything queued so far on the context stream
-    POTRF_TRY2(hipEventRecord(evfork, s) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "fork"));
-    POTRF_TRY2(hipStreamWaitEvent(sb, evfork, 0) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "fork"));
-    POTRF_TRY2(panel_work(0));
-    POTRF_TRY2(hipEventRecord(evp[0], s) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "event"));
-    for (int64_t k = 0; k + 1 < nt; ++k) {
-        if (k > 0) POTRF_TRY2(hipStreamWaitEvent(s, evr[(size_t)k - 1], 0) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "wait"));
-        POTRF_TRY2(launch_groups(k, GEMM_UPDATE, 1, s));
-        POTRF_TRY2(panel_work(k + 1));
-        POTRF_TRY2(hipEventRecord(evp[(size_t)k + 1], s) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "event"));
-        POTRF_TRY2(hipStreamWaitEvent(sb, evp[(size_t)k], 0) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "wait"));
-        POTRF_TRY2(launch_groups(k, GEMM_UPDATE, 0, sb));
-        POTRF_TRY2(hipEventRecord(evr[(size_t)k], sb) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "event"));
-    }
-    // join: the context stream waits for the last bulk update
-    if (nt > 1) POTRF_TRY2(hipStreamWaitEvent(s, evr[(size_t)nt - 2], 0) == hipSuccess ? GPEX_OK : set_err(ctx, GPEX_ERR_HIP, "join"));
+    auto schedule = [&]() -> int {
+        // fork: stream B starts after everything queued so far on the context stream
+        GPEX_TRY(record(evfork, s));
+        GPEX_TRY(wait(sb, evfork));
+        GPEX_TRY(panel_work(0));
+        GPEX_TRY(record(evp[0], s));
+        for (int64_t k = 0; k + 1 < nt; ++k) {
+            if (k > 0) GPEX_TRY(wait(s, evr[(size_t)k - 1]));
+            GPEX_TRY(launch_groups(k, GEMM_UPDATE, 1, s));
+            GPEX_TRY(panel_work(k + 1));
+            GPEX_TRY(record(evp[(size_t)k + 1], s));
+            GPEX_TRY(wait(sb, evp[(size_t)k]));
+            GPEX_TRY(launch_groups(k, GEMM_UPDATE, 0, sb));
+            GPEX_TRY(record(evr[(size_t)k], sb));
+        }
+        // join: the context stream waits for the last bulk update
+        if (nt > 1) GPEX_TRY(wait(s, evr[(size_t)nt - 2]));
+        return GPEX_OK;
+    };
+    int r = schedule();
     if (ctx->timing) {
         e_all1 = tm.next();
         (void)hipEventRecord(e_all1, s);
     }
     hipError_t se = hipStreamSynchronize(s);
-    if (se == hipSuccess) se = hipStreamSynchronize(sb);
-    release_sync();
-    if (se != hipSuccess) {
-        cleanup_all();
-        return set_err(ctx, GPEX_ERR_HIP, std::string("potrf sync: ") + hipGetErrorString(se));
-    }
+    if (two && se == hipSuccess) se = hipStreamSynchronize(sb);
+    if (r < 0) return r;
+    if (se != hipSuccess) return set_err(ctx, GPEX_ERR_HIP, std::string("potrf sync: ") + hipGetErrorString(se));
     if (ctx->timing) {
         float ms = 0;
         (void)hipEventElapsedTime(&ms, e_all0, e_all1);
@@ -543,24 +525,50 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             ctx->timings[1 + 3 * p] = 0;
             ctx->timings[2 + 3 * p] = 0;
             ctx->timings[3 + 3 * p] = upd_flops[(size_t)p];
+            ctx->timings[12 + p] = upd_flops_exact[(size_t)p];
         }
+        // per precision: summed launch durations and the busy time (union of the launch intervals,
+        // which overlap where launches of two streams run together)
+        std::vector<std::pair<double, double>> iv[3];
         for (auto& rc : recs) {
-            float m = 0;
+            float m = 0, b0 = 0, b1 = 0;
             (void)hipEventElapsedTime(&m, rc.b, rc.e);
+            (void)hipEventElapsedTime(&b0, e_all0, rc.b);
+            (void)hipEventElapsedTime(&b1, e_all0, rc.e);
             ctx->timings[1 + 3 * rc.prec] += m;
             ctx->timings[2 + 3 * rc.prec] += 1;
+            iv[rc.prec].push_back({b0, b1});
+        }
+        for (int p = 0; p < 3; ++p) {
+            std::sort(iv[p].begin(), iv[p].end());
+            double busy = 0, cb = -1, ce = -1;
+            for (auto& x : iv[p]) {
+                if (x.first > ce) {
+                    if (ce > cb) busy += ce - cb;
+                    cb = x.first;
+                    ce = x.second;
+                } else {
+                    ce = std::max(ce, x.second);
+                }
+            }
+            if (ce > cb) busy += ce - cb;
+            ctx->timings[15 + p] = busy;
         }
     }
-    long long fl = 0, bad = 0;
-    (void)hipMemcpy(&fl, ctx->d_flags + FLAG_INFO, sizeof(long long), hipMemcpyDeviceToHost);
-    (void)hipMemcpy(&bad, ctx->d_flags + FLAG_BADTASK, sizeof(long long), hipMemcpyDeviceToHost);
-    cleanup_all();
-    if (bad) return set_err(ctx, GPEX_ERR_STATE, "gpex_potrf_mp: internal task-type mismatch");
-    *info = fl;
+    long long fl[FLAG_COUNT] = {};
+    GPEX_HIP(ctx, hipMemcpy(fl, ctx->d_flags, sizeof(fl), hipMemcpyDeviceToHost));
+    if (fl[FLAG_BADTASK]) return set_err(ctx, GPEX_ERR_STATE, "gpex_potrf_mp: internal task-type mismatch");
+    *info = fl[FLAG_INFO];
+    if (fl[FLAG_INFO] != 0) {
+        // the tiles were overwritten in place up to the failing column: the handle is unusable
+        a->failed = true;
+        return set_err(ctx, GPEX_ERR_NOT_SPD, "gpex_potrf_mp: non-positive pivot at column " + std::to_string(fl[FLAG_INFO]));
+    }
     a->factored = true;
-    if (fl != 0) {
-        a->factored = false;
-        return set_err(ctx, GPEX_ERR_NOT_SPD, "gpex_potrf_mp: non-positive pivot at column " + std::to_string(fl));
+    if (fl[FLAG_FP16_OVF]) {
+        // a value stored in FP16 (an FP16 tile update or the FP16 copy of the factor) became +-inf
+        a->diag.fp16_overflow = 1;
+        return set_err(ctx, GPEX_WARN_FP16_OVERFLOW, "gpex_potrf_mp: an FP16 value of the factor overflowed");
     }
     return GPEX_OK;
 }

@@ -19,25 +19,46 @@ enum : int { FLAG_INFO = 0, FLAG_FP16_OVF = 1, FLAG_MSPE = 2, FLAG_BADTASK = 3, 
 
 }  // namespace gpex
 
+// Grow-only device workspaces kept by a context, one per entry point that needs temporaries.  A
+// call takes its slot's buffer (growing it when too small) and leaves it for the next call, so a
+// steady run allocates nothing; the buffers go back through the context's allocator at destroy
+// (or gpex_ctx_release_workspace).  Reuse is safe because every use is ordered on the context
+// stream (work forked to the context's other streams is joined back before a call returns).
+namespace gpex {
+enum : int { WS_COV = 0, WS_POTRF = 1, WS_SIM = 2, WS_KRIGE = 3, WS_SCAN = 4, WS_COUNT = 5 };
+}
+
 struct gpex_ctx_s {
     int device = 0;
     hipStream_t stream = nullptr;
     std::string err;
+    // device memory: the caller's allocator (e.g. torch's caching allocator), else hipMalloc
+    void* (*alloc)(size_t, void*) = nullptr;
+    void (*dealloc)(void*, void*) = nullptr;
+    void* user = nullptr;
     long long* d_flags = nullptr;     // FLAG_COUNT device words
     bool timing = false;
-    double timings[16] = {};          // layout documented at gpex_ctx_timings
-    // simulation workspace (FP16/FP64 input B, padded M, norm partials), kept between calls and
-    // grown when a call needs more
-    void* sim_ws = nullptr;
-    size_t sim_ws_bytes = 0;
+    bool serial = false;              // every launch on the context stream, in program order
+    double timings[32] = {};          // layout documented at gpex_ctx_timings
+    struct Ws {
+        void* p = nullptr;
+        size_t bytes = 0;
+    } ws[gpex::WS_COUNT];
     // side stream (default priority) for the ragged strips of a split GEMM launch, forked from and
     // joined to the launching stream through two events; created on first use
     hipStream_t side = nullptr;
     hipEvent_t side_fork = nullptr, side_join = nullptr;
+    // look-ahead stream of the factorization and its event pool (created on first use, kept)
+    hipStream_t ahead = nullptr;
+    std::vector<hipEvent_t> events;
 };
 
 struct gpex_tiled_s {
     int device = 0;
+    // the allocator of the creating context (the handle may outlive the context)
+    void* (*alloc)(size_t, void*) = nullptr;
+    void (*dealloc)(void*, void*) = nullptr;
+    void* user = nullptr;
     int64_t n = 0, nt = 0;
     int nb = 0;
     std::vector<uint8_t> map;        // nt*nt, row-major, 255 above the diagonal
@@ -52,6 +73,7 @@ struct gpex_tiled_s {
     _Float16* l16 = nullptr;
     _Float16* l16_panel(int64_t i) const { return l16 + (size_t)nb * nb * (size_t)(i * (i - 1) / 2); }
     bool factored = false;
+    bool failed = false;             // a factorization stopped at a non-positive pivot: tiles hold garbage
     gpex_prec_opts opts{};
     gpex_diag diag{};
 
@@ -79,8 +101,31 @@ int set_err(gpex_ctx_t ctx, int code, const std::string& msg);
         if (r_ < 0) return r_;       \
     } while (0)
 
+// Device memory through the context's allocator (hipMalloc / hipFree without one).  The tiled
+// variants use the allocator the handle recorded at creation.
 int dev_alloc(gpex_ctx_t ctx, void** p, size_t bytes, const char* what);
-void dev_free(void* p);
+void dev_free(gpex_ctx_t ctx, void* p);
+int tiled_alloc(gpex_ctx_t ctx, gpex_tiled_t t, void** p, size_t bytes, const char* what);
+void tiled_free(gpex_tiled_t t, void* p);
+// Workspace slot `slot` of at least `bytes` bytes (grown when smaller).
+int ws_get(gpex_ctx_t ctx, int slot, size_t bytes, void** out, const char* what);
+inline size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+// Consecutive 256-byte aligned pieces of one workspace buffer: size them with add(), then take
+// them in the same order from the buffer.
+struct Carve {
+    size_t total = 0;
+    std::vector<size_t> at;
+    size_t add(size_t b) {
+        at.push_back(total);
+        total += al256(b ? b : 1);
+        return at.size() - 1;
+    }
+    template <typename T> T* get(void* base, size_t piece) const {
+        return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + at[piece]);
+    }
+};
+// A timing-disabled event from the context's pool (index i, created on first use).
+int ctx_event(gpex_ctx_t ctx, size_t i, hipEvent_t* out);
 
 // ---- batched mixed-precision GEMM engine (gemm.hip) ---------------------------------------
 // One task: C (M x N) = alpha * op(A) * op(B) + beta * C.  op(A) is M x K, op(B) is K x N.
@@ -102,6 +147,11 @@ struct GemmTask {
     // written row-major, element (row, col) at C2[col + row * ldc2].
     _Float16* C2;
     int64_t ldc2;
+    // FP16 destination storage between k-tasks (simulation product only, whole blocks): the
+    // accumulator starts from beta C, is rounded to FP16 after every kround values of k and at the
+    // end of the K loop, and alpha times it is stored.  0: off.
+    int32_t kround;
+    int32_t pad3;
 };
 
 // Triangular structure of a task.  TRI_C_LOWER: only the lower triangle of C is wanted (blocks

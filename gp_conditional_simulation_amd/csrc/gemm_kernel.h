@@ -238,8 +238,10 @@ struct TSlab {
 // INTERLEAVE: products and memory instructions issued one by one (whole-block launches).  ROLE
 // only separates the symbols of trailing updates (1) and the simulation product (2) from the
 // other uses (0) so that kernel traces attribute their time.
+// EMU: FP16 destination storage between k-tasks (GemmTask::kround; FP32-accumulating compute
+// types, FP64 output, whole blocks only).
 template <typename CT, typename TA, typename TB, typename TC, int TRA, int TRB, bool EDGE, int ROLE,
-          int WMW = 2, int WNW = 2, int FJ = 4, int INTERLEAVE = 0>
+          int WMW = 2, int WNW = 2, int FJ = 4, int INTERLEAVE = 0, bool EMU = false>
 __global__ __launch_bounds__(64 * WMW * WNW)
 __attribute__((amdgpu_waves_per_eu(is_dyn<TA> ? 1 : 2, 2)))
 void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int bmc, int bnc, int m_off,
@@ -287,6 +289,39 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < FJ; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+    static_assert(!EMU || (!EDGE && sizeof(CT) <= 4 && std::is_same<TC, double>::value),
+                  "FP16 destination emulation: typed whole-block kernels with FP64 output");
+    if constexpr (EMU) {
+        // the destination enters the accumulator (it holds FP16 values: exact in FP32)
+        if (T.beta != 0.0) {
+            gptr<double> Cq = (gptr<double>)T.C;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = m0 + wm * 64 + i * 16 + l % 16;
+                        const int col = n0 + wn * WTN + j * 16 + acc_row<CT>(l, r);
+                        acc[i][j][r] = (float)(T.beta * Cq[(int64_t)row + (int64_t)col * T.ldc]);
+                    }
+        }
+    }
+    // round the accumulator to FP16 (the destination store of one k-task)
+    auto round16 = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < FJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[i][j][r] = (float)(_Float16)acc[i][j][r];
+    };
+    auto task_end = [&](int kb) {
+        if constexpr (EMU) {
+            if (((kb + 1) * BK) % T.kround == 0) round16();
+        }
+    };
 
     SA la;
     SB lb;
@@ -390,9 +425,16 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
         }
     };
     rd(As[0], Bs[0], 0, fa[0], fb[0]);
-    for (int kb = 0; kb + 2 < nk; ++kb) slab(kb, std::true_type{}, std::true_type{});
-    if (nk >= 2) slab(nk - 2, std::true_type{}, std::false_type{});
+    for (int kb = 0; kb + 2 < nk; ++kb) {
+        slab(kb, std::true_type{}, std::true_type{});
+        task_end(kb);
+    }
+    if (nk >= 2) {
+        slab(nk - 2, std::true_type{}, std::false_type{});
+        task_end(nk - 2);
+    }
     slab(nk - 1, std::false_type{}, std::false_type{});
+    if constexpr (EMU) round16();   // the end of the K loop ends the last task
 
     // Epilogue.  The operands went into the matrix cores as (B, A), so fragment (i, j) holds the
     // transposed 16 x 16 block: lane l is row l % 16 and register r is column acc_row(l, r).  The 16
@@ -400,7 +442,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     // each row group's old C values are all loaded before any store, so their latencies overlap.
     bool ovf = false;
     _Float16* __restrict__ C2 = T.C2;
-    const bool use_beta = T.beta != 0.0;
+    const bool use_beta = !EMU && T.beta != 0.0;   // EMU: the destination is in the accumulator
     auto epilogue = [&](auto out_tag) {   // out_tag: a value of the output element type
         typedef decltype(out_tag) TO;
         gptr_mut<TO> Cp = (gptr_mut<TO>)T.C;
@@ -469,6 +511,10 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     if (ovf && flags) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
 }
 
+static __global__ void k_flag_badtask(unsigned long long* flags) {
+    if (flags) atomicOr(&flags[FLAG_BADTASK], 1ull);
+}
+
 // Part of the output of a launch: bmc x bnc blocks of 128 x 128 from (m_off, n_off), in every task.
 struct Part {
     int m_off, n_off, bmc, bnc;
@@ -489,6 +535,14 @@ static int try_typed(hipStream_t s, const GemmTask* d_tasks, int ntasks, const G
     if (one.ta != DtOf<TA>::v || one.tb != DtOf<TB>::v || one.tc != DtOf<TC>::v) return 0;
     if (one.transA != TRA || (one.transB != 0) != (TRB != 0)) return 0;
     const unsigned grid = (unsigned)part_grid(p, ntasks, xcd);
+    if constexpr (ROLE == GEMM_TRMM && sizeof(CT) <= 4 && std::is_same<TC, double>::value) {
+        if (one.kround) {   // FP16 destination emulation: 128 x 128 blocks, whole blocks only
+            if (!p.fast) return 0;
+            hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, false, ROLE, 2, 2, 4, 1, true>), dim3(grid), dim3(NTHR),
+                               0, s, d_tasks, one, ntasks, p.bmc, p.bnc, p.m_off, p.n_off, xcd, fl);
+            return 1;
+        }
+    }
     if (!p.fast) {
         if constexpr (RAGGED) {
             hipLaunchKernelGGL((k_gemm_t<CT, TA, TB, TC, TRA, TRB, true, ROLE>), dim3(grid), dim3(NTHR), 0, s, d_tasks,
@@ -571,6 +625,10 @@ static void launch_part(hipStream_t s, const GemmTask* d_tasks, int ntasks, cons
         if (!done) done = try_update_row<CT, _Float16>(s, d_tasks, ntasks, one, p, xcd, fl);
     }
     if (done) return;
+    if (one.kround) {   // no kernel emulates FP16 destinations for this shape: flag it, compute nothing
+        hipLaunchKernelGGL(k_flag_badtask, dim3(1), dim3(1), 0, s, fl);
+        return;
+    }
     // everything else: element types read from the tasks, bounds-checked element loads
     const dim3 grid((unsigned)part_grid(p, ntasks, xcd));
     switch ((one.transA ? 2 : 0) | (one.transB ? 1 : 0)) {
@@ -614,6 +672,11 @@ static int launch_ct(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int
     } else if ((int64_t)mw * nw * ntasks < 512) {
         // few whole blocks: one bounds-checked launch costs less than three on the critical path
         launch_part<CT, ROLE>(s, d_tasks, ntasks, one, Part{0, 0, bmc, bnc, false}, xcd, fl);
+    } else if (ctx->serial) {
+        // serial mode: the same three launches, one after the other on the launching stream
+        if (mw < bmc) launch_part<CT, ROLE>(s, d_tasks, ntasks, one, Part{mw * BM, 0, 1, bnc, false}, xcd, fl);
+        if (nw < bnc) launch_part<CT, ROLE>(s, d_tasks, ntasks, one, Part{0, nw * BN, mw, 1, false}, xcd, fl);
+        launch_part<CT, ROLE>(s, d_tasks, ntasks, one, Part{0, 0, mw, nw, true}, xcd, fl);
     } else {
         // the strips run beside the whole blocks on the context's side stream
         if (!ctx->side) {

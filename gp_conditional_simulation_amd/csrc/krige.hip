@@ -102,7 +102,8 @@ static unsigned nblk(int64_t n) { return (unsigned)((n + 255) / 256); }
 // Step k applies T_k (or T_k^T) to block row k, then subtracts its contribution from every block
 // row still to be solved in one batched launch (the full-height rows; a ragged last row of tiles
 // gets a launch of its own).
-static int tile_trsm(gpex_ctx_t ctx, gpex_tiled_t L, double* B, int64_t ldb, int64_t m, int trans, double* tmp) {
+static int tile_trsm(gpex_ctx_t ctx, gpex_tiled_t L, double* B, int64_t ldb, int64_t m, int trans, double* tmp,
+                     GemmTask* d_tasks) {
     const int64_t nt = L->nt, nb = L->nb, n = L->n;
     hipStream_t s = ctx->stream;
     auto rows = [&](int64_t k) { return std::min<int64_t>(nb, n - k * nb); };
@@ -131,14 +132,9 @@ static int tile_trsm(gpex_ctx_t ctx, gpex_tiled_t L, double* B, int64_t ldb, int
         st.b1 = (int64_t)tasks.size();
         steps.push_back(st);
     }
-    GemmTask* d_tasks = nullptr;
-    if (!tasks.empty()) {
-        GPEX_TRY(dev_alloc(ctx, (void**)&d_tasks, sizeof(GemmTask) * tasks.size(), "solve tasks"));
-        if (hipMemcpy(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice) != hipSuccess) {
-            dev_free(d_tasks);
-            return set_err(ctx, GPEX_ERR_HIP, "solve task upload");
-        }
-    }
+    // d_tasks holds nt (nt - 1) / 2 tasks; the upload is ordered after the previous solve's launches
+    if (!tasks.empty())
+        GPEX_HIP(ctx, hipMemcpyAsync(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice, s));
     int r = GPEX_OK;
     for (const Step& st : steps) {
         const int64_t k = st.k, rk = rows(k);
@@ -160,11 +156,8 @@ static int tile_trsm(gpex_ctx_t ctx, gpex_tiled_t L, double* B, int64_t ldb, int
         }
         if (r < 0) break;
     }
-    // the task list is released once the queued launches no longer read it
-    if (d_tasks) {
-        if (hipStreamSynchronize(s) != hipSuccess && r >= 0) r = set_err(ctx, GPEX_ERR_HIP, "solve sync");
-        dev_free(d_tasks);
-    }
+    // the host task list must outlive its upload
+    if (hipStreamSynchronize(s) != hipSuccess && r >= 0) r = set_err(ctx, GPEX_ERR_HIP, "solve sync");
     return r;
 }
 
@@ -197,19 +190,24 @@ extern "C" int gpex_krige(gpex_ctx_t ctx, const double* d_loc_o, int64_t n_o, co
     }
     const int64_t ntile = Sy->nt;
     const int64_t rows_pad = ntile * nb;
-    double *Vop = nullptr, *Xo = nullptr, *F = nullptr, *G = nullptr, *H = nullptr, *tmp = nullptr;
-    auto cleanup = [&]() {
-        dev_free(Vop); dev_free(Xo); dev_free(F); dev_free(G); dev_free(H); dev_free(tmp);
-        gpex_tiled_destroy(Sy);
-    };
+    auto cleanup = [&]() { gpex_tiled_destroy(Sy); };
     const int64_t mtmp = std::max<int64_t>(n_p, 3);
-    r = dev_alloc(ctx, (void**)&Vop, sizeof(double) * n_o * n_p, "V_op copy");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&tmp, sizeof(double) * nb * mtmp, "solve scratch");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&Xo, sizeof(double) * rows_pad * 3, "X_o");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&F, sizeof(double) * n_o * 3, "F");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&G, sizeof(double) * 9, "G");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&H, sizeof(double) * 3 * n_p, "H");
+    // workspace: V_op, the solve scratch, X_o, F, G, H and the solve task list
+    Carve cv;
+    const size_t p_vop = cv.add(sizeof(double) * n_o * n_p), p_tmp = cv.add(sizeof(double) * nb * mtmp),
+                 p_xo = cv.add(sizeof(double) * rows_pad * 3), p_f = cv.add(sizeof(double) * n_o * 3),
+                 p_g = cv.add(sizeof(double) * 9), p_h = cv.add(sizeof(double) * 3 * n_p),
+                 p_tk = cv.add(sizeof(GemmTask) * (size_t)(ntile * (ntile - 1) / 2));
+    void* wsb = nullptr;
+    r = ws_get(ctx, WS_KRIGE, cv.total, &wsb, "kriging workspace");
     if (r < 0) { cleanup(); return r; }
+    double* Vop = cv.get<double>(wsb, p_vop);
+    double* tmp = cv.get<double>(wsb, p_tmp);
+    double* Xo = cv.get<double>(wsb, p_xo);
+    double* F = cv.get<double>(wsb, p_f);
+    double* G = cv.get<double>(wsb, p_g);
+    double* H = cv.get<double>(wsb, p_h);
+    GemmTask* d_tk = cv.get<GemmTask>(wsb, p_tk);
     CovK ck{params->kind, params->sigma2, params->range, params->nu};
     hipLaunchKernelGGL(k_cov_cross, dim3(nblk(n_o * n_p)), dim3(256), 0, s, d_loc_o, n_o, d_loc_p, n_p, ck, Vop);
     hipLaunchKernelGGL(k_design, dim3(nblk(rows_pad)), dim3(256), 0, s, d_loc_o, n_o, rows_pad, Xo, rows_pad);
@@ -219,8 +217,8 @@ extern "C" int gpex_krige(gpex_ctx_t ctx, const double* d_loc_o, int64_t n_o, co
     if (k_trend == 3) {
         // F = Sigma_y^-1 X_o
         r = copy2d(ctx, s, Xo, DT_F64, rows_pad, F, DT_F64, n_o, n_o, 3, 1.0);
-        if (r >= 0) r = tile_trsm(ctx, Sy, F, n_o, 3, 0, tmp);
-        if (r >= 0) r = tile_trsm(ctx, Sy, F, n_o, 3, 1, tmp);
+        if (r >= 0) r = tile_trsm(ctx, Sy, F, n_o, 3, 0, tmp, d_tk);
+        if (r >= 0) r = tile_trsm(ctx, Sy, F, n_o, 3, 1, tmp, d_tk);
         // G = X_o^T F (3 x 3);  Rhs = F^T V_op (3 x n_p) into H
         if (r >= 0) r = gemm1(ctx, DT_F64, Xo, DT_F64, 1, rows_pad, F, DT_F64, 0, n_o, G, DT_F64, 3, 3, 3, (int)n_o, 1.0, 0.0);
         if (r >= 0) r = gemm1(ctx, DT_F64, F, DT_F64, 1, n_o, Vop, DT_F64, 0, n_o, H, DT_F64, 3, 3, (int)n_p, (int)n_o, 1.0, 0.0);
@@ -261,8 +259,8 @@ extern "C" int gpex_krige(gpex_ctx_t ctx, const double* d_loc_o, int64_t n_o, co
         if (hipGetLastError() != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "trend launch"); }
     }
     // L_o Y = V_op - X_o H;  L_o^T W = Y
-    r = tile_trsm(ctx, Sy, d_W, n_o, n_p, 0, tmp);
-    if (r >= 0) r = tile_trsm(ctx, Sy, d_W, n_o, n_p, 1, tmp);
+    r = tile_trsm(ctx, Sy, d_W, n_o, n_p, 0, tmp, d_tk);
+    if (r >= 0) r = tile_trsm(ctx, Sy, d_W, n_o, n_p, 1, tmp, d_tk);
     // zhat = W^T y_o
     if (r >= 0) r = gemm1(ctx, DT_F64, d_W, DT_F64, 1, n_o, d_y_o, DT_F64, 0, n_o, d_zhat, DT_F64, n_p, (int)n_p, 1, (int)n_o, 1.0, 0.0);
     if (r < 0) { cleanup(); return r; }

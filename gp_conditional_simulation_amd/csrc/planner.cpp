@@ -7,6 +7,8 @@
 //              Eq. 11 relative magnitude of the FP16 tiles;
 //   Sec. V-E   Eq. 12: l_f = sqrt(x_min,norm / v_min), u_f = sqrt(x_max / v_max) over present
 //              reduced formats, u_s = min(65504, min_f u_f), s = floor(u_s) - 1 when that exceeds 1.
+//   Algorithm 1 casts the scaled factor to FP16; |(L_s)_ij| <= s sqrt(V_ii) adds the bound
+//              u_L = 65504 / sqrt(max_i V_ii) to u_s (it binds only when max_i V_ii > 1).
 // Readings where the page is silent or garbled: the tile rule r * NT * eps_p <= tol with
 // r = ||V_ij||_F / ||V||_F and NT tile rows (the unscaled r * eps_p <= tol on request);
 // Eq. 11 as max(rho1, rho2) < 1e-4/2^-10;
@@ -102,9 +104,14 @@ static void plan_once(const std::vector<double>& st, int64_t nt, const gpex_prec
         lsub = std::fmax(lsub, lsf);
         umin = std::fmin(umin, uf);
     }
+    // The simulation product casts L_s to FP16 (Algorithm 1), and |(L_s)_ij| <= s sqrt(V_ii): the
+    // factor stays finite in FP16 when s <= x_max,FP16 / sqrt(max_i V_ii).
+    double vmax_diag = -INFINITY;
+    for (int64_t i = 0; i < nt; ++i) vmax_diag = std::fmax(vmax_diag, T(i, i)[2]);
+    d.u_factor = vmax_diag > 0.0 ? xmax16 / std::sqrt(vmax_diag) : INFINITY;
     d.l_bound = l;
     d.l_bound_sub = lsub;
-    d.u_bound = std::fmin(65504.0, umin);
+    d.u_bound = std::fmin(std::fmin(65504.0, umin), d.u_factor);
     d.lower_exceeds_upper = l > d.u_bound;
     double sc = std::floor(d.u_bound) - 1.0;
     d.s = sc > 1.0 ? sc : 1.0;

@@ -70,10 +70,11 @@ __global__ void k_normals(uint64_t seed, uint32_t stream, int64_t n, int64_t nsi
 // l = j n + i).  Per-block partial sums of (Z/s)^2 go to part.  The padding is k_zero_pad's.
 __global__ __launch_bounds__(256) void k_make_B(const double* Zin, int64_t n, int64_t nsim,
                                                 uint64_t seed, int64_t rows_pad, double inv_s, int amp,
-                                                void* B, double* part) {
+                                                void* B, double* part, unsigned long long* flags) {
     const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = n * nsim;
     double sq = 0.0;
+    bool ovf = false;
     if (2 * p < total) {
         double z[2];
         if (Zin) {
@@ -89,10 +90,16 @@ __global__ __launch_bounds__(256) void k_make_B(const double* Zin, int64_t n, in
             const double b = amp ? z[e] * inv_s : z[e];
             sq += b * b;
             const int64_t at = l % n + (l / n) * rows_pad;
-            if (amp) static_cast<_Float16*>(B)[at] = f64_to_f16(b);
-            else static_cast<double*>(B)[at] = b;
+            if (amp) {
+                const _Float16 h = f64_to_f16(b);
+                ovf |= __builtin_isinf((float)h) && !__builtin_isinf(b);
+                static_cast<_Float16*>(B)[at] = h;
+            } else {
+                static_cast<double*>(B)[at] = b;
+            }
         }
     }
+    if (ovf) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
     __shared__ double red[256];
     red[threadIdx.x] = sq;
     __syncthreads();
@@ -118,92 +125,115 @@ __global__ void k_zero_pad(int64_t n, int64_t nsim, int64_t rows_pad, int64_t co
 }
 
 // ---- scan ------------------------------------------------------------------------------------
-constexpr int SR = 128, SC = 64;   // rows x columns per scan workgroup
+constexpr int SROWS = 256, SCOLS = 64;   // rows of a scan tile (one per thread), columns of a block
+constexpr int SCAN_MAX_GROUPS = 256;     // row groups: per-(group, column) partials
 
-// Per workgroup: rows [rb*SR, +SR) x columns [cb*SC, +SC) of S.  Phase 1 (thread = row, half of
-// the columns): coalesced column reads, exceedance counts per row (one atomic per row and
-// workgroup), >=/<= flags to LDS.  Phase 2 (thread = column, quarter of the rows): min of t over
-// the >= set, max over the <= set, size of the >= set -> per-(row block, column) partials.
+// Workgroup (g, cb) scans the row tiles g, g + G, g + 2G, ... of column block cb (SCOLS columns).
+// Phase 1, thread = row: reads the row's SCOLS values of S (each column read by 256 consecutive
+// rows: whole cache lines), adds its exceedance count to counts[row] (one atomic per row and
+// block) and leaves the >= / <= flags of the row as two 64-bit masks in LDS.  Phase 2, thread =
+// (column, quarter of the rows): min of t over the >= rows, max over the <= rows, size of the >=
+// set, kept in registers across the group's tiles.  The quarters are folded in order at the end
+// and written as the group's partials of each column; k_scan_finish folds the groups in order.
+// Rows beyond np and columns beyond nsim carry no flags.
 __global__ __launch_bounds__(256) void k_scan(const double* __restrict__ S, int64_t lds, int64_t np,
-                                              int64_t nsim, const double* __restrict__ t, double u,
+                                              int64_t nsim, const double* __restrict__ t, double u, int G,
                                               unsigned long long* __restrict__ counts,
                                               double* __restrict__ psi_part, double* __restrict__ phi_part,
                                               int* __restrict__ size_part) {
-    __shared__ uint8_t ge[SR][SC + 1], le[SR][SC + 1];
-    __shared__ double ts[SR];
-    __shared__ int cnt2[SR];
-    __shared__ double red_mn[4][SC], red_mx[4][SC];
-    __shared__ int red_sz[4][SC];
+    __shared__ uint64_t ge[SROWS], le[SROWS];
+    __shared__ double ts[SROWS];
+    __shared__ double red_mn[4][SCOLS], red_mx[4][SCOLS];
+    __shared__ int red_sz[4][SCOLS];
     const int tid = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.x * SR, c0 = (int64_t)blockIdx.y * SC;
-    {
-        int r = tid % SR, half = tid / SR;
-        int64_t gr = r0 + r;
-        int cnt = 0;
-        for (int c = half * (SC / 2); c < (half + 1) * (SC / 2); ++c) {
-            int64_t gc = c0 + c;
-            uint8_t g = 0, e = 0;
-            if (gr < np && gc < nsim) {
-                double v = S[gr + gc * lds];
-                g = v >= u;
-                e = v <= u;
+    const int g = blockIdx.x;
+    const int64_t c0 = (int64_t)blockIdx.y * SCOLS;
+    const int ncol = (int)(nsim - c0 < SCOLS ? nsim - c0 : SCOLS);
+    const int64_t nrt = (np + SROWS - 1) / SROWS;
+    const int c = tid % SCOLS, q = tid / SCOLS;
+    double mn = INFINITY, mx = -INFINITY;
+    int sz = 0;
+    for (int64_t rt = g; rt < nrt; rt += G) {
+        const int64_t gr = rt * SROWS + tid;
+        uint64_t fg = 0, fe = 0;
+        if (gr < np) {
+            const double* col = S + gr + c0 * lds;
+            int cnt = 0;
+#pragma unroll 16
+            for (int cc = 0; cc < SCOLS; ++cc) {
+                if (cc < ncol) {
+                    const double v = col[cc * lds];
+                    const bool a = v >= u, b = v <= u;
+                    fg |= (uint64_t)a << cc;
+                    fe |= (uint64_t)b << cc;
+                    cnt += a;
+                }
             }
-            ge[r][c] = g;
-            le[r][c] = e;
-            cnt += g;
+            if (cnt) atomicAdd(&counts[gr], (unsigned long long)cnt);
+            ts[tid] = t ? t[gr] : 0.0;
         }
-        if (half == 1) cnt2[r] = cnt;
-        if (half == 0) ts[r] = (t && gr < np) ? t[gr] : 0.0;
+        ge[tid] = fg;
+        le[tid] = fe;
         __syncthreads();
-        if (half == 0 && gr < np) {
-            int tot = cnt + cnt2[r];
-            if (tot) atomicAdd(&counts[gr], (unsigned long long)tot);
-        }
-    }
-    __syncthreads();
-    {
-        int c = tid % SC, q = tid / SC;
-        double mn = INFINITY, mx = -INFINITY;
-        int sz = 0;
-        for (int r = q * (SR / 4); r < (q + 1) * (SR / 4); ++r) {
-            if (ge[r][c]) {
+#pragma unroll 8
+        for (int r = q * (SROWS / 4); r < (q + 1) * (SROWS / 4); ++r) {
+            const uint64_t a = ge[r], b = le[r];
+            const double tr = ts[r];
+            if ((a >> c) & 1u) {
                 sz += 1;
-                mn = fmin(mn, ts[r]);
+                mn = fmin(mn, tr);
             }
-            if (le[r][c]) mx = fmax(mx, ts[r]);
+            if ((b >> c) & 1u) mx = fmax(mx, tr);
         }
-        red_mn[q][c] = mn;
-        red_mx[q][c] = mx;
-        red_sz[q][c] = sz;
         __syncthreads();
-        if (q == 0 && c0 + c < nsim) {
-            for (int k = 1; k < 4; ++k) {
-                mn = fmin(mn, red_mn[k][c]);
-                mx = fmax(mx, red_mx[k][c]);
-                sz += red_sz[k][c];
-            }
-            int64_t o = (int64_t)blockIdx.x * nsim + c0 + c;
-            psi_part[o] = mn;
-            phi_part[o] = mx;
-            size_part[o] = sz;
+    }
+    red_mn[q][c] = mn;
+    red_mx[q][c] = mx;
+    red_sz[q][c] = sz;
+    __syncthreads();
+    if (q == 0 && c < ncol) {
+        for (int k = 1; k < 4; ++k) {
+            mn = fmin(mn, red_mn[k][c]);
+            mx = fmax(mx, red_mx[k][c]);
+            sz += red_sz[k][c];
         }
+        const int64_t o = (int64_t)g * nsim + c0 + c;
+        psi_part[o] = mn;
+        phi_part[o] = mx;
+        size_part[o] = sz;
     }
 }
 
+// Column j: fold the G group partials in group order.
 __global__ void k_scan_finish(const double* psi_part, const double* phi_part, const int* size_part,
-                              int64_t nrb, int64_t nsim, double* psi, double* phi, int* sizes) {
-    int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+                              int G, int64_t nsim, double* psi, double* phi, int* sizes) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= nsim) return;
     double mn = INFINITY, mx = -INFINITY;
     int sz = 0;
-    for (int64_t b = 0; b < nrb; ++b) {
-        mn = fmin(mn, psi_part[b * nsim + j]);
-        mx = fmax(mx, phi_part[b * nsim + j]);
-        sz += size_part[b * nsim + j];
+    for (int b = 0; b < G; ++b) {
+        mn = fmin(mn, psi_part[(int64_t)b * nsim + j]);
+        mx = fmax(mx, phi_part[(int64_t)b * nsim + j]);
+        sz += size_part[(int64_t)b * nsim + j];
     }
     psi[j] = mn;
     phi[j] = mx;
     sizes[j] = sz;
+}
+
+// Row groups of a scan: enough workgroups to fill the GPU (2048), at most one per row tile and
+// at most SCAN_MAX_GROUPS.
+static int scan_groups(int64_t np, int64_t nsim) {
+    const int64_t nrt = (np + SROWS - 1) / SROWS, ncb = (nsim + SCOLS - 1) / SCOLS;
+    int64_t G = (2048 + ncb - 1) / ncb;
+    if (G > nrt) G = nrt;
+    if (G > SCAN_MAX_GROUPS) G = SCAN_MAX_GROUPS;
+    return (int)(G < 1 ? 1 : G);
+}
+
+__global__ void k_fill_i64(int64_t* a, int64_t n, int64_t v) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) a[i] = v;
 }
 
 // t = (zhat - u) / sqrt(v) (Eq. 1); a non-positive v raises the MSPE flag.
@@ -236,11 +266,6 @@ __global__ void k_regions(const double* t, int64_t np, double q_in, double q_out
     double ti = t[i];
     cout[i] = ti >= q_out;
     cin[i] = ti > q_in;
-}
-
-__global__ void k_u64_to_i64(const unsigned long long* a, int64_t* b, int64_t n) {
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) b[i] = (int64_t)a[i];
 }
 
 static unsigned blocks(int64_t n, int t = 256) { return (unsigned)((n + t - 1) / t); }
@@ -276,6 +301,7 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     if (!ctx) return GPEX_ERR_ARG;
     if (!L || !d_M || nsim < 1 || ldm < (L ? L->n : 0))
         return set_err(ctx, GPEX_ERR_ARG, "gpex_trmm_sim: bad argument (handle, d_M, nsim or ldm)");
+    if (L->failed) return set_err(ctx, GPEX_ERR_STATE, "gpex_trmm_sim: the factorization of this matrix failed");
     if (!L->factored) return set_err(ctx, GPEX_ERR_STATE, "gpex_trmm_sim: matrix is not factored");
     GPEX_HIP(ctx, hipSetDevice(ctx->device));
     hipStream_t s = ctx->stream;
@@ -283,29 +309,12 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     const int64_t rows = nt * nb;
     const int64_t cols = ((nsim + 127) / 128) * 128;
     const int amp = L->opts.amp ? 1 : 0;
-    void* B = nullptr;
-    double* Mp = nullptr;
-    double* part = nullptr;
-    GemmTask* d_tasks = nullptr;
-    auto cleanup = [&]() { dev_free(d_tasks); };
+    // FP16 destination storage between the k-tasks of Algorithm 1 (the pages' default path)
+    const int emu = amp && L->opts.fp16_dest_emulation ? 1 : 0;
+    if (emu && nb % 128 != 0)
+        return set_err(ctx, GPEX_ERR_ARG, "gpex_trmm_sim: FP16 destination emulation needs a tile size that is a multiple of 128");
     const int64_t nblkB = (n * nsim / 2 + 1 + 255) / 256;   // k_make_B: one thread per element pair
     const int64_t npad = (rows - n) * nsim + rows * (cols - nsim);
-    auto al256 = [](size_t b) { return (b + 255) / 256 * 256; };
-    const size_t bB = al256((size_t)rows * cols * (amp ? 2 : 8)), bM = al256(sizeof(double) * rows * cols),
-                 bP = al256(sizeof(double) * nblkB);
-    int r = GPEX_OK;
-    if (ctx->sim_ws_bytes < bB + bM + bP) {   // the previous call has completed: it synchronised
-        dev_free(ctx->sim_ws);
-        ctx->sim_ws = nullptr;
-        ctx->sim_ws_bytes = 0;
-        r = dev_alloc(ctx, &ctx->sim_ws, bB + bM + bP, "simulation workspace");
-        if (r >= 0) ctx->sim_ws_bytes = bB + bM + bP;
-    }
-    if (r >= 0) {
-        B = ctx->sim_ws;
-        Mp = reinterpret_cast<double*>(static_cast<uint8_t*>(ctx->sim_ws) + bB);
-        part = reinterpret_cast<double*>(static_cast<uint8_t*>(ctx->sim_ws) + bB + bM);
-    }
     // An all-FP64 factor whose tiles of each row are stored back to back (column-major nb x nb
     // tiles with no alignment gap): the off-diagonal tiles of row i then form one column-major
     // nb x (i nb) matrix with leading dimension nb, so the row's whole contribution is one product.
@@ -316,66 +325,39 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
                          (j == 0 || static_cast<uint8_t*>(L->tile(i, j)) ==
                                         static_cast<uint8_t*>(L->tile(i, j - 1)) + (size_t)nb * nb * 8);
     const bool fused = (amp && L->l16) || rowpanel64;
-    // otherwise: off-diagonal tasks for every step, built once and grouped by the factor tile's
-    // storage type (one typed kernel per launch)
-    struct Group { int64_t b0, b1; };
-    std::vector<GemmTask> tasks;
-    std::vector<Group> groups;
-    std::vector<int64_t> gbeg((size_t)nt + 1, 0);
-    for (int64_t k = 0; k < nt && !fused; ++k) {
-        gbeg[(size_t)k] = (int64_t)groups.size();
-        for (int ta = DT_F64; ta <= DT_F16; ++ta) {
-            int64_t b0 = (int64_t)tasks.size();
-            for (int64_t i = k + 1; i < nt; ++i) {
-                if (L->prec(i, k) != ta) continue;
-                GemmTask g{};
-                g.A = L->tile(i, k); g.ta = (int8_t)ta; g.lda = nb; g.transA = 0;
-                g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
-                g.ldb = rows; g.transB = 0;
-                g.C = Mp + i * nb; g.tc = DT_F64; g.ldc = rows;
-                g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
-                g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
-                tasks.push_back(g);
-            }
-            if ((int64_t)tasks.size() > b0) groups.push_back(Group{b0, (int64_t)tasks.size()});
-        }
-    }
-    gbeg[(size_t)nt] = (int64_t)groups.size();
-    if (r >= 0 && !tasks.empty()) {
-        r = dev_alloc(ctx, (void**)&d_tasks, sizeof(GemmTask) * tasks.size(), "trmm tasks");
-        if (r >= 0 && hipMemcpy(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice) != hipSuccess)
-            r = set_err(ctx, GPEX_ERR_HIP, "trmm task upload");
-    }
-    if (r >= 0 && hipMemsetAsync(ctx->d_flags + FLAG_BADTASK, 0, sizeof(long long), s) != hipSuccess)
-        r = set_err(ctx, GPEX_ERR_HIP, "trmm flag reset");
-    if (r < 0) { cleanup(); return r; }
-    hipEvent_t ev[4] = {};
-    std::vector<hipEvent_t> kev;
-    if (ctx->timing) {
-        for (auto& e : ev) (void)hipEventCreate(&e);
-        (void)hipEventRecord(ev[0], s);
-    }
-    hipLaunchKernelGGL(k_make_B, dim3((unsigned)nblkB), dim3(256), 0, s, d_Z, n, nsim, seed, rows,
-                       1.0 / L->s, amp, B, part);
-    if (npad > 0)
-        hipLaunchKernelGGL(k_zero_pad, dim3((unsigned)((npad + 255) / 256)), dim3(256), 0, s, n, nsim, rows, cols, amp, B);
-    if (hipGetLastError() != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "make_B launch"); }
-    if (ctx->timing) (void)hipEventRecord(ev[1], s);
+    // workspace: the input B, the padded M, the norm partials and the task list
+    const size_t ntask = fused ? (size_t)(2 * nt) : (size_t)(nt * (nt + 1) / 2);
+    Carve cv;
+    const size_t p_B = cv.add((size_t)rows * cols * (amp ? 2 : 8)), p_M = cv.add(sizeof(double) * rows * cols),
+                 p_part = cv.add(sizeof(double) * nblkB), p_tasks = cv.add(sizeof(GemmTask) * ntask);
+    void* wsb = nullptr;
+    GPEX_TRY(ws_get(ctx, WS_SIM, cv.total, &wsb, "simulation workspace"));
+    void* B = cv.get<void>(wsb, p_B);
+    double* Mp = cv.get<double>(wsb, p_M);
+    double* part = cv.get<double>(wsb, p_part);
+    GemmTask* d_tasks = cv.get<GemmTask>(wsb, p_tasks);
+    auto* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
+    const int32_t kround = emu ? (int32_t)nb : 0;
+
+    std::vector<GemmTask> tasks;   // uploaded once; alive until the final synchronisation
+    // diagonal tiles: FP32 products of cast32(L_kk) and cast32(B_k) (mixed precision) or FP64
+    auto diag_task = [&](int64_t k, double beta) {
+        GemmTask g{};
+        g.A = L->tile(k, k); g.ta = DT_F64; g.lda = nb; g.transA = 0;
+        g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
+        g.ldb = rows; g.transB = 0;
+        g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
+        g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
+        g.alpha = 1.0; g.beta = beta;
+        g.tri = TRI_A_LOWER;   // L_kk is lower triangular
+        g.kround = kround;     // cast16 of the diagonal product (Algorithm 1)
+        return g;
+    };
+    struct Launch { int64_t b0, b1; int compute; };
+    std::vector<Launch> launches;
     if (fused) {
-        // diagonal tiles, one launch: FP32 products of cast32(L_kk) and cast32(B_k) (mixed
-        // precision) or FP64 products
-        std::vector<GemmTask> dg;
-        for (int64_t k = 0; k < nt; ++k) {
-            GemmTask g{};
-            g.A = L->tile(k, k); g.ta = DT_F64; g.lda = nb; g.transA = 0;
-            g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
-            g.ldb = rows; g.transB = 0;
-            g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
-            g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
-            g.alpha = 1.0; g.beta = 0.0;
-            g.tri = TRI_A_LOWER;   // L_kk is lower triangular
-            dg.push_back(g);
-        }
+        for (int64_t k = 0; k < nt; ++k) tasks.push_back(diag_task(k, 0.0));
+        launches.push_back(Launch{0, nt, amp ? DT_F32 : DT_F64});
         // off-diagonal part of tile row i: one product of the row panel (nb x i nb) with
         // B[0 : i nb], longest rows first: FP16 (the row-major cast16 panels) or FP64 (the tiles)
         std::vector<GemmTask> od;
@@ -390,6 +372,7 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
             g.C = Mp + i * nb; g.tc = DT_F64; g.ldc = rows;
             g.M = (int)nb; g.N = (int)cols; g.K = (int)(i * nb);
             g.alpha = 1.0; g.beta = 1.0;
+            g.kround = kround;   // GEMM16 stores its destination in FP16 after each k-task
             od.push_back(g);
         }
         // Task t of a batched launch runs on XCD t mod 8.  Reversing every second group of eight
@@ -397,151 +380,176 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         // XCD 0 gets the longest row of every group (15% above the mean at 98 tile rows).
         for (size_t g0 = 8; g0 < od.size(); g0 += 16)
             std::reverse(od.begin() + (std::ptrdiff_t)g0, od.begin() + (std::ptrdiff_t)std::min(g0 + 8, od.size()));
-        GemmTask* d2 = nullptr;
-        r = dev_alloc(ctx, (void**)&d2, sizeof(GemmTask) * (dg.size() + od.size()), "trmm panel tasks");
-        if (r >= 0 && hipMemcpy(d2, dg.data(), sizeof(GemmTask) * dg.size(), hipMemcpyHostToDevice) != hipSuccess)
-            r = set_err(ctx, GPEX_ERR_HIP, "trmm task upload");
-        if (r >= 0 && !od.empty() &&
-            hipMemcpy(d2 + dg.size(), od.data(), sizeof(GemmTask) * od.size(), hipMemcpyHostToDevice) != hipSuccess)
-            r = set_err(ctx, GPEX_ERR_HIP, "trmm task upload");
-        if (r >= 0) r = gemm_launch(ctx, s, amp ? DT_F32 : DT_F64, d2, (int)dg.size(), dg[0], GEMM_TRMM);
-        if (r >= 0 && !od.empty())
-            r = gemm_launch(ctx, s, amp ? DT_F16 : DT_F64, d2 + dg.size(), (int)od.size(), od[0], GEMM_TRMM);
-        // d2 is released after the stream synchronisation below
-        dev_free(d_tasks);
-        d_tasks = d2;
-        if (r < 0) { cleanup(); return r; }
-    } else {
-        for (int64_t k = 0; k < nt; ++k) {
-            GemmTask g{};
-            g.A = L->tile(k, k); g.ta = DT_F64; g.lda = nb; g.transA = 0;
-            g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
-            g.ldb = rows; g.transB = 0;
-            g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
-            g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
-            g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
-            g.tri = TRI_A_LOWER;   // L_kk is lower triangular
-            r = gemm_launch(ctx, s, amp ? DT_F32 : DT_F64, nullptr, 1, g, GEMM_TRMM);
-            for (int64_t gi = gbeg[(size_t)k]; r >= 0 && gi < gbeg[(size_t)k + 1]; ++gi) {
-                const Group& G = groups[(size_t)gi];
-                r = gemm_launch(ctx, s, amp ? DT_F16 : DT_F64, d_tasks + G.b0, (int)(G.b1 - G.b0), tasks[(size_t)G.b0],
-                                GEMM_TRMM);
-            }
-            if (r < 0) { cleanup(); return r; }
+        if (!od.empty()) {
+            launches.push_back(Launch{(int64_t)tasks.size(), (int64_t)(tasks.size() + od.size()), amp ? DT_F16 : DT_F64});
+            tasks.insert(tasks.end(), od.begin(), od.end());
         }
+    } else {
+        // per step k: the diagonal tile, then the tiles below it, grouped by the factor tile's
+        // storage type (one typed kernel per launch)
+        for (int64_t k = 0; k < nt; ++k) {
+            tasks.push_back(diag_task(k, k == 0 ? 0.0 : 1.0));
+            launches.push_back(Launch{(int64_t)tasks.size() - 1, (int64_t)tasks.size(), amp ? DT_F32 : DT_F64});
+            for (int ta = DT_F64; ta <= DT_F16; ++ta) {
+                const int64_t b0 = (int64_t)tasks.size();
+                for (int64_t i = k + 1; i < nt; ++i) {
+                    if (L->prec(i, k) != ta) continue;
+                    GemmTask g{};
+                    g.A = L->tile(i, k); g.ta = (int8_t)ta; g.lda = nb; g.transA = 0;
+                    g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
+                    g.ldb = rows; g.transB = 0;
+                    g.C = Mp + i * nb; g.tc = DT_F64; g.ldc = rows;
+                    g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
+                    g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
+                    tasks.push_back(g);
+                }
+                if ((int64_t)tasks.size() > b0) launches.push_back(Launch{b0, (int64_t)tasks.size(), amp ? DT_F16 : DT_F64});
+            }
+        }
+    }
+    if (tasks.size() > ntask) return set_err(ctx, GPEX_ERR_STATE, "gpex_trmm_sim: task count exceeds its workspace");
+    GPEX_HIP(ctx, hipMemcpyAsync(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice, s));
+    GPEX_HIP(ctx, hipMemsetAsync(ctx->d_flags + FLAG_FP16_OVF, 0, sizeof(long long) * (FLAG_BADTASK - FLAG_FP16_OVF + 1), s));
+    hipEvent_t ev[6] = {};
+    if (ctx->timing) {
+        for (auto& e : ev) (void)hipEventCreate(&e);
+        (void)hipEventRecord(ev[0], s);
+    }
+    hipLaunchKernelGGL(k_make_B, dim3((unsigned)nblkB), dim3(256), 0, s, d_Z, n, nsim, seed, rows,
+                       1.0 / L->s, amp, B, part, fl);
+    if (npad > 0)
+        hipLaunchKernelGGL(k_zero_pad, dim3((unsigned)((npad + 255) / 256)), dim3(256), 0, s, n, nsim, rows, cols, amp, B);
+    GPEX_HIP(ctx, hipGetLastError());
+    if (ctx->timing) (void)hipEventRecord(ev[1], s);
+    int r = GPEX_OK;
+    for (size_t q = 0; q < launches.size() && r >= 0; ++q) {
+        const Launch& Lq = launches[q];
+        if (ctx->timing && fused && q == 1) (void)hipEventRecord(ev[4], s);
+        r = gemm_launch(ctx, s, Lq.compute, d_tasks + Lq.b0, (int)(Lq.b1 - Lq.b0), tasks[(size_t)Lq.b0], GEMM_TRMM);
+        if (ctx->timing && fused && q == 1) (void)hipEventRecord(ev[5], s);
     }
     if (ctx->timing) (void)hipEventRecord(ev[2], s);
-    r = copy2d(ctx, s, Mp, DT_F64, rows, d_M, DT_F64, ldm, n, nsim, 1.0);
+    if (r >= 0) r = copy2d(ctx, s, Mp, DT_F64, rows, d_M, DT_F64, ldm, n, nsim, 1.0);
     if (ctx->timing) (void)hipEventRecord(ev[3], s);
-    if (r < 0) { cleanup(); return r; }
-    long long bad = 0;
-    if (diag || ctx->timing) {
-        std::vector<double> h((size_t)nblkB);
-        hipError_t e = hipMemcpyAsync(h.data(), part, sizeof(double) * nblkB, hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipMemcpyAsync(&bad, ctx->d_flags + FLAG_BADTASK, sizeof(long long), hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "trmm sync"); }
-        double ss = 0.0;
-        for (double v : h) ss += v;
-        if (diag) {
-            *diag = L->diag;
-            diag->norm_B = std::sqrt(ss);
-        }
-        if (ctx->timing) {
-            float a = 0, b = 0;
-            (void)hipEventElapsedTime(&a, ev[0], ev[3]);
-            (void)hipEventElapsedTime(&b, ev[1], ev[2]);
-            ctx->timings[10] = a;
-            ctx->timings[11] = b;
-            for (auto& e2 : ev) (void)hipEventDestroy(e2);
-        }
-    } else {
-        // buffers are freed below; make sure the queued work no longer needs them
-        hipError_t e = hipMemcpyAsync(&bad, ctx->d_flags + FLAG_BADTASK, sizeof(long long), hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipStreamSynchronize(s);
-        if (e != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "trmm sync"); }
+    std::vector<double> h((size_t)nblkB);
+    long long flags[FLAG_COUNT] = {};
+    hipError_t e = hipMemcpyAsync(h.data(), part, sizeof(double) * nblkB, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(flags, ctx->d_flags, sizeof(flags), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);   // also keeps `tasks` alive for its upload
+    if (r < 0) return r;
+    if (e != hipSuccess) return set_err(ctx, GPEX_ERR_HIP, std::string("trmm sync: ") + hipGetErrorString(e));
+    if (ctx->timing) {
+        float a = 0, b = 0, c = 0;
+        (void)hipEventElapsedTime(&a, ev[0], ev[3]);
+        (void)hipEventElapsedTime(&b, ev[1], ev[2]);
+        if (fused && launches.size() > 1) (void)hipEventElapsedTime(&c, ev[4], ev[5]);
+        ctx->timings[10] = a;
+        ctx->timings[11] = b;
+        ctx->timings[18] = c;
+        for (auto& e2 : ev) (void)hipEventDestroy(e2);
     }
-    cleanup();
-    if (bad) return set_err(ctx, GPEX_ERR_STATE, "gpex_trmm_sim: internal task-type mismatch");
+    double ss = 0.0;
+    for (double v : h) ss += v;
+    if (diag) {
+        *diag = L->diag;
+        diag->norm_B = std::sqrt(ss);
+        diag->fp16_overflow = flags[FLAG_FP16_OVF] ? 1 : 0;
+    }
+    if (flags[FLAG_BADTASK]) return set_err(ctx, GPEX_ERR_STATE, "gpex_trmm_sim: internal task-type mismatch");
+    if (flags[FLAG_FP16_OVF])
+        return set_err(ctx, GPEX_WARN_FP16_OVERFLOW, "gpex_trmm_sim: an entry of Z / s overflowed in FP16");
     return GPEX_OK;
 }
 
-extern "C" int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p,
-                                      int64_t n_o, int64_t nsim, const double* d_W, const double* d_y_o,
-                                      const double* d_zhat, const double* d_v, double u, double level_c,
-                                      int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
-                                      uint8_t* d_cin, uint8_t* d_cout, double* d_S, gpex_region_stats* st) {
-    if (!ctx) return GPEX_ERR_ARG;
+// Device temporaries of one gpex_excursion_regions call (S and the residual only when n_o > 0).
+struct ScanMem {
+    double *S, *R, *t, *pp, *pq, *psi, *phi;
+    int* sp;
+};
+
+static void scan_carve(Carve& cv, int64_t n_p, int64_t n_o, int64_t nsim, bool need_S, size_t piece[8]) {
+    const int G = scan_groups(n_p, nsim);
+    piece[0] = cv.add(need_S ? sizeof(double) * n_p * nsim : 0);
+    piece[1] = cv.add(n_o > 0 ? sizeof(double) * n_o * nsim : 0);
+    piece[2] = cv.add(sizeof(double) * n_p);
+    piece[3] = cv.add(sizeof(double) * G * nsim);
+    piece[4] = cv.add(sizeof(double) * G * nsim);
+    piece[5] = cv.add(sizeof(int) * G * nsim);
+    piece[6] = cv.add(sizeof(double) * nsim);
+    piece[7] = cv.add(sizeof(double) * nsim);
+}
+
+static ScanMem scan_mem(const Carve& cv, void* base, const size_t piece[8]) {
+    ScanMem m{};
+    m.S = cv.get<double>(base, piece[0]);
+    m.R = cv.get<double>(base, piece[1]);
+    m.t = cv.get<double>(base, piece[2]);
+    m.pp = cv.get<double>(base, piece[3]);
+    m.pq = cv.get<double>(base, piece[4]);
+    m.sp = cv.get<int>(base, piece[5]);
+    m.psi = cv.get<double>(base, piece[6]);
+    m.phi = cv.get<double>(base, piece[7]);
+    return m;
+}
+
+static int excursion_check(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p, int64_t n_o, int64_t nsim,
+                           const double* d_W, const double* d_y_o, const double* d_zhat, const double* d_v,
+                           double level_c, int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
+                           uint8_t* d_cin, uint8_t* d_cout) {
     if (!d_M || n_p < 1 || n_o < 0 || nsim < 1 || ldm < n_p + n_o || !d_counts || !d_sizes)
         return set_err(ctx, GPEX_ERR_ARG, "gpex_excursion_regions: bad sizes or null M/counts/sizes");
     if (n_o > 0 && (!d_W || !d_y_o))
         return set_err(ctx, GPEX_ERR_ARG, "gpex_excursion_regions: W and y_o are needed when n_o > 0");
-    const bool regions = d_zhat != nullptr;
-    if (regions && (!d_v || !h_psi || !h_phi || !d_cin || !d_cout))
+    if (d_zhat && (!d_v || !h_psi || !h_phi || !d_cin || !d_cout))
         return set_err(ctx, GPEX_ERR_ARG, "gpex_excursion_regions: v, psi, phi, cin, cout are needed with zhat");
-    if (regions && !(level_c > 0.0 && level_c < 1.0))
+    if (d_zhat && !(level_c > 0.0 && level_c < 1.0))
         return set_err(ctx, GPEX_ERR_ARG, "gpex_excursion_regions: level must lie in (0, 1)");
-    GPEX_HIP(ctx, hipSetDevice(ctx->device));
+    return GPEX_OK;
+}
+
+// Conditioning, scan and calibration on the temporaries m (S and R used only when n_o > 0 and,
+// for S, d_S is NULL).
+static int excursion_run(gpex_ctx_t ctx, const ScanMem& m, const double* d_M, int64_t ldm, int64_t n_p, int64_t n_o,
+                         int64_t nsim, const double* d_W, const double* d_y_o, const double* d_zhat,
+                         const double* d_v, double u, double level_c, int64_t* d_counts, int32_t* d_sizes,
+                         double* h_psi, double* h_phi, uint8_t* d_cin, uint8_t* d_cout, double* d_S,
+                         gpex_region_stats* st) {
     hipStream_t s = ctx->stream;
     auto* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
-    double *Sbuf = nullptr, *R = nullptr, *t = nullptr, *pp = nullptr, *pq = nullptr, *psi = nullptr, *phi = nullptr;
-    int* sp = nullptr;
-    unsigned long long* cnt = nullptr;
-    auto cleanup = [&]() {
-        if (!d_S) dev_free(Sbuf);
-        dev_free(R); dev_free(t); dev_free(pp); dev_free(pq); dev_free(psi); dev_free(phi);
-        dev_free(sp); dev_free(cnt);
-    };
-    int r = GPEX_OK;
+    const bool regions = d_zhat != nullptr;
     const double* S = d_M;
     int64_t lds = ldm;
     if (n_o > 0) {
-        if (d_S) Sbuf = d_S;
-        else r = dev_alloc(ctx, (void**)&Sbuf, sizeof(double) * n_p * nsim, "S");
-        if (r >= 0) r = dev_alloc(ctx, (void**)&R, sizeof(double) * n_o * nsim, "residual");
-        if (r >= 0) r = copy2d(ctx, s, d_M, DT_F64, ldm, Sbuf, DT_F64, n_p, n_p, nsim, 1.0);
-        if (r >= 0) {
-            hipLaunchKernelGGL(k_residual, dim3(blocks(n_o * nsim)), dim3(256), 0, s, d_M, ldm, n_p, n_o, nsim, d_y_o, R);
-            if (hipGetLastError() != hipSuccess) r = set_err(ctx, GPEX_ERR_HIP, "residual launch");
-        }
-        if (r >= 0)
-            r = gemm1(ctx, DT_F64, d_W, DT_F64, 1, n_o, R, DT_F64, 0, n_o, Sbuf, DT_F64, n_p,
-                      (int)n_p, (int)nsim, (int)n_o, 1.0, 1.0);
+        double* Sbuf = d_S ? d_S : m.S;
+        GPEX_TRY(copy2d(ctx, s, d_M, DT_F64, ldm, Sbuf, DT_F64, n_p, n_p, nsim, 1.0));
+        hipLaunchKernelGGL(k_residual, dim3(blocks(n_o * nsim)), dim3(256), 0, s, d_M, ldm, n_p, n_o, nsim, d_y_o, m.R);
+        GPEX_HIP(ctx, hipGetLastError());
+        GPEX_TRY(gemm1(ctx, DT_F64, d_W, DT_F64, 1, n_o, m.R, DT_F64, 0, n_o, Sbuf, DT_F64, n_p, (int)n_p, (int)nsim,
+                       (int)n_o, 1.0, 1.0));
         S = Sbuf;
         lds = n_p;
     } else if (d_S) {
-        r = copy2d(ctx, s, d_M, DT_F64, ldm, d_S, DT_F64, n_p, n_p, nsim, 1.0);
+        GPEX_TRY(copy2d(ctx, s, d_M, DT_F64, ldm, d_S, DT_F64, n_p, n_p, nsim, 1.0));
     }
-    const int64_t nrb = (n_p + SR - 1) / SR, ncb = (nsim + SC - 1) / SC;
-    if (r >= 0) r = dev_alloc(ctx, (void**)&t, sizeof(double) * n_p, "t");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&pp, sizeof(double) * nrb * nsim, "psi partials");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&pq, sizeof(double) * nrb * nsim, "phi partials");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&sp, sizeof(int) * nrb * nsim, "size partials");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&psi, sizeof(double) * nsim, "psi");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&phi, sizeof(double) * nsim, "phi");
-    if (r >= 0) r = dev_alloc(ctx, (void**)&cnt, sizeof(unsigned long long) * n_p, "counts");
-    if (r < 0) { cleanup(); return r; }
-    hipError_t e = hipMemsetAsync(cnt, 0, sizeof(unsigned long long) * n_p, s);
-    if (e == hipSuccess) e = hipMemsetAsync(ctx->d_flags + FLAG_MSPE, 0, sizeof(long long), s);
-    if (e != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "scan setup"); }
-    if (regions) hipLaunchKernelGGL(k_tstat, dim3(blocks(n_p)), dim3(256), 0, s, d_zhat, d_v, u, n_p, t, fl);
-    hipLaunchKernelGGL(k_scan, dim3((unsigned)nrb, (unsigned)ncb), dim3(256), 0, s, S, lds, n_p, nsim,
-                       regions ? t : nullptr, u, cnt, pp, pq, sp);
-    hipLaunchKernelGGL(k_scan_finish, dim3(blocks(nsim)), dim3(256), 0, s, pp, pq, sp, nrb, nsim, psi, phi, d_sizes);
-    hipLaunchKernelGGL(k_u64_to_i64, dim3(blocks(n_p)), dim3(256), 0, s, cnt, d_counts, n_p);
-    if (hipGetLastError() != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "scan launch"); }
-    if (!regions) {
-        // the temporaries are released below; wait for the queued kernels that read them
-        if (hipStreamSynchronize(s) != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "scan sync"); }
-        cleanup();
-        return GPEX_OK;
-    }
+    const int G = scan_groups(n_p, nsim);
+    const int64_t ncb = (nsim + SCOLS - 1) / SCOLS;
+    hipLaunchKernelGGL(k_fill_i64, dim3(blocks(n_p)), dim3(256), 0, s, d_counts, n_p, (int64_t)0);
+    hipLaunchKernelGGL(k_fill_i64, dim3(1), dim3(1), 0, s, reinterpret_cast<int64_t*>(ctx->d_flags + FLAG_MSPE),
+                       (int64_t)1, (int64_t)0);
+    if (regions) hipLaunchKernelGGL(k_tstat, dim3(blocks(n_p)), dim3(256), 0, s, d_zhat, d_v, u, n_p, m.t, fl);
+    hipLaunchKernelGGL(k_scan, dim3((unsigned)G, (unsigned)ncb), dim3(256), 0, s, S, lds, n_p, nsim,
+                       regions ? m.t : nullptr, u, G, reinterpret_cast<unsigned long long*>(d_counts), m.pp, m.pq,
+                       m.sp);
+    hipLaunchKernelGGL(k_scan_finish, dim3(blocks(nsim)), dim3(256), 0, s, m.pp, m.pq, m.sp, G, nsim, m.psi, m.phi,
+                       d_sizes);
+    GPEX_HIP(ctx, hipGetLastError());
+    if (!regions) return GPEX_OK;   // counts and sizes are queued on the context stream
     long long mflag = 0;
-    e = hipMemcpyAsync(h_psi, psi, sizeof(double) * nsim, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipMemcpyAsync(h_phi, phi, sizeof(double) * nsim, hipMemcpyDeviceToHost, s);
+    hipError_t e = hipMemcpyAsync(h_psi, m.psi, sizeof(double) * nsim, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(h_phi, m.phi, sizeof(double) * nsim, hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipMemcpyAsync(&mflag, ctx->d_flags + FLAG_MSPE, sizeof(long long), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "psi/phi copy"); }
+    if (e != hipSuccess) return set_err(ctx, GPEX_ERR_HIP, "psi/phi copy");
     // host: gather, sort each sample without its sentinel, Eq. 9
     std::vector<double> a, b;
     for (int64_t j = 0; j < nsim; ++j) {
@@ -556,22 +564,38 @@ extern "C" int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t
     rs.q_out = rs.q_in = NAN;
     if (mflag) {
         if (st) *st = rs;
-        cleanup();
         return set_err(ctx, GPEX_ERR_MSPE_NONPOS, "gpex_excursion_regions: some MSPE v_i <= 0");
     }
     if (a.empty() || b.empty()) {
         if (st) *st = rs;
-        cleanup();
         return set_err(ctx, GPEX_ERR_EMPTY_SAMPLE, "gpex_excursion_regions: psi or phi sample is empty");
     }
     double alpha = std::round((1.0 - level_c) * 1e6) / 1e6;
     rs.q_out = a[(size_t)(quantile_index(alpha, rs.n_psi) - 1)];
     rs.q_in = b[(size_t)(quantile_index(1.0 - alpha, rs.n_phi) - 1)];
-    hipLaunchKernelGGL(k_regions, dim3(blocks(n_p)), dim3(256), 0, s, t, n_p, rs.q_in, rs.q_out, d_cin, d_cout);
+    hipLaunchKernelGGL(k_regions, dim3(blocks(n_p)), dim3(256), 0, s, m.t, n_p, rs.q_in, rs.q_out, d_cin, d_cout);
     e = hipGetLastError();
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    cleanup();
     if (e != hipSuccess) return set_err(ctx, GPEX_ERR_HIP, "regions");
     if (st) *st = rs;
     return GPEX_OK;
 }
+
+extern "C" int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p,
+                                      int64_t n_o, int64_t nsim, const double* d_W, const double* d_y_o,
+                                      const double* d_zhat, const double* d_v, double u, double level_c,
+                                      int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
+                                      uint8_t* d_cin, uint8_t* d_cout, double* d_S, gpex_region_stats* st) {
+    if (!ctx) return GPEX_ERR_ARG;
+    GPEX_TRY(excursion_check(ctx, d_M, ldm, n_p, n_o, nsim, d_W, d_y_o, d_zhat, d_v, level_c, d_counts, d_sizes,
+                             h_psi, h_phi, d_cin, d_cout));
+    GPEX_HIP(ctx, hipSetDevice(ctx->device));
+    Carve cv;
+    size_t piece[8];
+    scan_carve(cv, n_p, n_o, nsim, n_o > 0 && !d_S, piece);
+    void* wsb = nullptr;
+    GPEX_TRY(ws_get(ctx, WS_SCAN, cv.total, &wsb, "scan workspace"));
+    return excursion_run(ctx, scan_mem(cv, wsb, piece), d_M, ldm, n_p, n_o, nsim, d_W, d_y_o, d_zhat, d_v, u, level_c,
+                         d_counts, d_sizes, h_psi, h_phi, d_cin, d_cout, d_S, st);
+}
+

@@ -15,6 +15,10 @@
  *   - Pointers named d_* are device pointers owned by the caller (for example torch tensors
  *     on the context's device); pointers named h_* are host pointers owned by the caller.
  *     The library never frees caller memory.
+ *   - Device memory the library needs (tile storage and the factor's FP16 copy, owned by a tiled
+ *     handle; grow-only workspaces and flags, owned by the context) comes from the allocator given
+ *     at context creation, or from hipMalloc / hipFree when none is given.  A context keeps its
+ *     workspaces between calls, so repeated calls of the same sizes allocate nothing.
  *   - Matrices are column-major with an explicit leading dimension; vectors are contiguous.
  *   - All device work is enqueued on the stream given at context creation.  Entry points that
  *     return host values (info, diagnostics, psi/phi, region statistics) synchronise that
@@ -31,6 +35,7 @@
 #ifndef GPEX_H
 #define GPEX_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -69,13 +74,19 @@ typedef struct {
  * FP64; unscaled_rule != 0 drops the NT factor (r * eps <= tol).  tol is the pages' fixedacc.
  * auto_tol != 0 (automatic mode, Sec. V-D): tol starts at 1e-4 (the given tol is ignored) and is
  * multiplied by 0.9 while Eq. 10 or Eq. 11 fails and FP16 tiles remain (at most 2000 rounds);
- * the final tol and the number of reductions are reported in gpex_diag. */
+ * the final tol and the number of reductions are reported in gpex_diag.
+ * fp16_dest_emulation != 0 (amp = 1 only; the tile size must be a multiple of 128): the
+ * simulation product keeps its destination in FP16 between k-tasks as Algorithm 1 does (the
+ * diagonal product is rounded to FP16, then after each off-diagonal tile k the running sum is
+ * rounded to FP16), each task accumulating in FP32.  Default 0: one FP32 sum over the whole row
+ * added to the FP64 result (more accurate, Sec. V-F leaves the accumulation to the platform). */
 typedef struct {
     int amp;
     double tol;
     int allow_fp16;
     int unscaled_rule;
     int auto_tol;
+    int fp16_dest_emulation;
 } gpex_prec_opts;
 
 /* Diagnostics of the plan (Sec. V-D, V-E) and of the simulation input (Algorithm 1). */
@@ -83,7 +94,7 @@ typedef struct {
     double s;             /* applied covariance scale, Eq. 12 (1 when unscaled) */
     double frob;          /* ||V||_F of the unscaled matrix */
     double l_bound;       /* l = max_f l_f (normal-range lower bound) */
-    double u_bound;       /* u_s = min(65504, min_f u_f) */
+    double u_bound;       /* u_s = min(65504, min_f u_f, u_factor) */
     double l_bound_sub;   /* lower bound with the subnormal limits (reported when l > u_s) */
     double r_hp;          /* Eq. 10 ratio v_max^HP / v_min^HP (NaN without FP16 tiles) */
     double rho1, rho2;    /* Eq. 11 ratios */
@@ -92,6 +103,8 @@ typedef struct {
     int64_t tiles[3];     /* lower tiles per precision: FP64, FP32, FP16 */
     double tol;           /* tolerance the map was built with (the final one in automatic mode) */
     int64_t tol_reductions; /* automatic mode: number of 0.9 reductions applied */
+    double u_factor;      /* 65504 / sqrt(max_i V_ii): u_s also stays below it, so that the FP16
+                             cast of L_s (Algorithm 1) stays finite (|(L_s)_ij| <= s sqrt(V_ii)) */
 } gpex_diag;
 
 typedef struct {
@@ -101,14 +114,32 @@ typedef struct {
 
 /* ---- context ------------------------------------------------------------------------------ */
 /* Binds HIP device `device` and the stream `hip_stream` (a hipStream_t; NULL = null stream).
+ * alloc / dealloc (both given or both NULL) supply device memory: alloc(bytes, user) returns a
+ * device pointer (NULL when out of memory: the entry point then returns GPEX_ERR_NOMEM) and
+ * dealloc(ptr, user) releases it.  The allocator must be ordered on hip_stream (memory released
+ * after queued work may be handed out again only to work queued after it, as torch's caching
+ * allocator does for its stream); without one the library uses hipMalloc / hipFree.
  * *out receives the context.  Every entry point queues its work on that stream and, where it
  * forks work onto streams of its own (the factorization's look-ahead stream, the context's side
- * stream for the ragged edges of large GEMM launches, created on first use, default priority),
- * joins them back to it with events before returning.  Errors: GPEX_ERR_ARG, GPEX_ERR_HIP. */
-int gpex_ctx_create(int device, void* hip_stream, gpex_ctx_t* out);
+ * stream for the ragged edges of large GEMM launches; both created on first use, default
+ * priority), joins them back to it with events before returning.  Errors: GPEX_ERR_ARG,
+ * GPEX_ERR_HIP, GPEX_ERR_NOMEM. */
+int gpex_ctx_create(int device, void* hip_stream, void* (*alloc)(size_t, void*),
+                    void (*dealloc)(void*, void*), void* user, gpex_ctx_t* out);
 /* Synchronises the context's streams and releases everything the context owns (flags, the
- * simulation workspace, the side stream and its events).  Errors: GPEX_ERR_ARG. */
+ * workspaces, the extra streams and their events).  Tiled handles keep working after their
+ * context is destroyed only for gpex_tiled_info / gpex_tiled_stats / gpex_tiled_destroy.
+ * Errors: GPEX_ERR_ARG. */
 int gpex_ctx_destroy(gpex_ctx_t ctx);
+/* Synchronises the context stream and releases the context's workspaces (they are taken again,
+ * at the size the next call needs, by the next call).  Errors: GPEX_ERR_ARG, GPEX_ERR_HIP. */
+int gpex_ctx_release_workspace(gpex_ctx_t ctx);
+/* on != 0: serial schedule.  Every launch runs on the context stream in program order: the
+ * factorization's look-ahead stream and the side stream of split GEMM launches are not used.
+ * Each tile receives the same operations in the same order and from the same kernels as in
+ * the concurrent schedule, so results are bitwise identical; the switch exists to check that.
+ * Errors: GPEX_ERR_ARG. */
+int gpex_ctx_set_serial(gpex_ctx_t ctx, int on);
 /* Text of the last non-OK status on this context (valid until the next call on it). */
 const char* gpex_last_error(gpex_ctx_t ctx);
 /* Library version string. */
@@ -157,14 +188,31 @@ int gpex_tiled_to_dense(gpex_ctx_t ctx, gpex_tiled_t t, double* d_out, int64_t l
  * Used to check leading blocks and sampled rows of large factors.  Enqueued on ctx. */
 int gpex_tiled_block(gpex_ctx_t ctx, gpex_tiled_t t, int64_t r0, int64_t c0, int64_t rows,
                      int64_t cols, double* d_out, int64_t ld);
+/* Raw values of a block, converted exactly to FP64 with no unscaling: which = 0 reads the stored
+ * tiles (s^2 V before the factorisation, L_s after it; entries above the diagonal tiles read 0),
+ * which = 1 the FP16 copy of the off-diagonal factor tiles that the simulation product multiplies
+ * with (Algorithm 1, cast16 of L_s; entries in diagonal tiles and above read 0; needs a factor
+ * computed with amp = 1, else GPEX_ERR_STATE).  Lets a caller check that every stored value is a
+ * value of its tile's precision and that the FP16 copy is cast16 of the stored factor.  Block
+ * bounds and ld as in gpex_tiled_block.  Enqueued on ctx. */
+int gpex_tiled_block_raw(gpex_ctx_t ctx, gpex_tiled_t t, int which, int64_t r0, int64_t c0, int64_t rows,
+                         int64_t cols, double* d_out, int64_t ld);
 int gpex_tiled_destroy(gpex_tiled_t t);
 
 /* ---- mixed-precision tile Cholesky ------------------------------------------------------- */
-/* Factors the tiled matrix in place: s^2 V = L_s L_s^T, keeping the precision map (diagonal
- * POTRF in FP64; a panel tile is solved in its own precision, FP16 tiles computed in FP32;
- * a trailing tile is updated in its own precision with operands converted to it; FP16 updates
- * use FP16 matrix cores with FP32 accumulation).  *info = 0, or the 1-based column of the first
- * non-positive pivot (then GPEX_ERR_NOT_SPD).  Synchronises. */
+/* Factors the tiled matrix in place, s^2 V = L_s L_s^T (Sec. IV-B; Algorithm 2, step 12), keeping
+ * the precision map.  Step k: the diagonal tile is factored in FP64 together with its explicit
+ * inverse T_k; every panel tile (i, k) is solved as A_ik T_k^T on FP64 matrix cores and rounded
+ * once to its own precision (a reduced-precision solve through T_k loses definiteness on strongly
+ * correlated covariances); every trailing tile is updated in its own precision with the operands
+ * converted to it (FP16 tiles on FP16 matrix cores with FP32 accumulation and one FP16 rounding per
+ * update), diagonal tiles in FP64.  With amp = 1 the panel solves also write the FP16 copy of
+ * each off-diagonal factor tile that gpex_trmm_sim multiplies with (Algorithm 1, cast16).
+ * *info = 0, or the 1-based column of the first non-positive pivot: then GPEX_ERR_NOT_SPD and the
+ * handle is marked failed (its tiles were overwritten in place): gpex_potrf_mp, gpex_trmm_sim,
+ * gpex_tiled_block and gpex_tiled_to_dense then return GPEX_ERR_STATE.  GPEX_WARN_FP16_OVERFLOW
+ * (the factor is usable, diag.fp16_overflow set) when a value stored in FP16 became +-inf.
+ * Synchronises. */
 int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info);
 
 /* ---- simulation --------------------------------------------------------------------------- */
@@ -180,11 +228,14 @@ int gpex_normals(gpex_ctx_t ctx, uint64_t seed, uint32_t stream, int64_t n, int6
  * the explicit d_Z (n x nsim, leading dimension n) or, when d_Z is NULL, the seeded normals of
  * gpex_normals(seed, stream 0).  With amp = 1, B is rounded to FP16, each off-diagonal L tile
  * is converted to FP16 and multiplied on FP16 matrix cores, the diagonal tile is applied in
- * FP32, all with FP32 accumulation, and M is written in FP64; with amp = 0 everything is FP64.
- * d_M: n x nsim, leading dimension ldm >= n.  diag (may be NULL) receives norm_B.
- * Requires a factored matrix (GPEX_ERR_STATE otherwise).  Synchronises before returning.
- * The context keeps the workspace of its largest call (the FP16 or FP64 input B and a padded
- * copy of M: about (2 or 8) + 8 bytes per element of the padded n x nsim) until it is destroyed. */
+ * FP32, all with FP32 accumulation, and M is written in FP64 (with fp16_dest_emulation the
+ * running sum is kept in FP16 between k-tasks, see gpex_prec_opts); with amp = 0 everything is
+ * FP64.  d_M: n x nsim, leading dimension ldm >= n.  diag (may be NULL) receives the plan's
+ * diagnostics with norm_B.  Requires a factored matrix (GPEX_ERR_STATE otherwise).  Returns
+ * GPEX_WARN_FP16_OVERFLOW (M is written) when an entry of Z / s overflowed in FP16.
+ * Synchronises before returning.  The context keeps the workspace of its largest call (the FP16
+ * or FP64 input B and a padded copy of M: about (2 or 8) + 8 bytes per element of the padded
+ * n x nsim) until it is destroyed or its workspace released. */
 int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t l, int64_t nsim, uint64_t seed, const double* d_Z,
                   double* d_M, int64_t ldm, gpex_diag* diag);
 
@@ -212,7 +263,10 @@ int gpex_krige(gpex_ctx_t ctx, const double* d_loc_o, int64_t n_o, const double*
  * d_M: (n_p + n_o) x nsim, leading dimension ldm, prediction rows first.  d_W (n_o x n_p, ld
  * n_o) and d_y_o are needed when n_o > 0.  d_S (may be NULL) receives S (n_p x nsim, ld n_p).
  * Returns GPEX_ERR_MSPE_NONPOS when some v_i <= 0 and GPEX_ERR_EMPTY_SAMPLE when a sample is
- * empty (counts and psi/phi are still written).  Synchronises when d_zhat is given. */
+ * empty (counts and psi/phi are still written).  Synchronises when d_zhat is given; otherwise
+ * the counts and sizes are queued on the context stream and the call returns at once.
+ * Temporaries (S when d_S is NULL and n_o > 0, the residual, t, per-group partials) live in a
+ * context workspace. */
 int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p,
                            int64_t n_o, int64_t nsim, const double* d_W, const double* d_y_o,
                            const double* d_zhat, const double* d_v, double u, double level_c,
@@ -221,15 +275,21 @@ int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64
 
 /* ---- timing support ------------------------------------------------------------------------ */
 /* Per-phase device time of the last gpex_potrf_mp / gpex_trmm_sim on ctx, measured with HIP
- * events recorded on the context stream around the launches (enable with
- * gpex_ctx_set_timing(ctx, 1); it adds event records and no synchronisation).  out[16]:
+ * events recorded around the launches on the streams they run on (enable with
+ * gpex_ctx_set_timing(ctx, 1); it adds event records and no synchronisation).  out[32]:
  *   [0] potrf total ms;
- *   [1..3] trailing-update launches computing in FP64: summed ms, launch count, algorithmic flops
- *          (2 nb^3 per off-diagonal tile, nb^3 per diagonal tile);
+ *   [1..3] trailing-update launches computing in FP64: summed launch ms, launch count, flops on
+ *          whole tiles (2 nb^3 per off-diagonal tile, nb^3 per diagonal tile);
  *   [4..6] the same for FP32 launches, [7..9] for FP16 launches;
- *   [10] trmm total ms, [11] trmm matrix-core launches ms; [12..15] reserved (0). */
+ *   [10] trmm total ms, [11] trmm matrix-core launches ms;
+ *   [12..14] trailing-update flops per precision (FP64, FP32, FP16) on the tiles' true sizes
+ *          (the last tile row and column hold n - (NT - 1) nb rows);
+ *   [15..17] busy ms of the trailing-update launches per precision: the union of their launch
+ *          intervals (launches of the two streams overlap, so [1], [4], [7] may exceed it);
+ *   [18] trmm: ms of the off-diagonal (row-panel) launch of the simulation product;
+ *   [19..31] reserved (0). */
 int gpex_ctx_set_timing(gpex_ctx_t ctx, int on);
-int gpex_ctx_timings(gpex_ctx_t ctx, double* out16);
+int gpex_ctx_timings(gpex_ctx_t ctx, double* out32);
 
 #ifdef __cplusplus
 }

@@ -31,6 +31,7 @@ _dv = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 _i64 = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
 _i32 = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 _u32 = np.ctypeslib.ndpointer(dtype=np.uint32, flags="C_CONTIGUOUS")
+_u8 = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
 
 
 def lib():
@@ -59,6 +60,11 @@ def lib():
         L.orc_scan.argtypes = [_d, I64, I64, I64, C.c_void_p, D, _i64, _i32, C.c_void_p, C.c_void_p]
         L.orc_philox4x32_10.argtypes = [_u32, _u32, _u32]
         L.orc_normals.argtypes = [C.c_uint64, C.c_uint32, I64, I64, I64, I64, I64, _d, I64]
+        L.orc_round_fp16.restype = D
+        L.orc_round_fp16.argtypes = [D]
+        L.orc_potrf_mp_emul.restype = I64
+        L.orc_potrf_mp_emul.argtypes = [_d, I64, I64, I64, _u8]
+        L.orc_trmm_mp_emul.argtypes = [_d, I64, I64, I64, D, _d, I64, I64, I, _d, I64]
         _lib = L
     return _lib
 
@@ -208,3 +214,31 @@ def normals(seed: int, stream: int, n: int, nsim: int, rows=None, cols=None) -> 
     out = np.empty((i1 - i0, j1 - j0), order="F")
     lib().orc_normals(seed, stream, n, i0, i1, j0, j1, out, max(i1 - i0, 1))
     return out
+
+
+def round_fp16(x: float) -> float:
+    """Nearest IEEE binary16 value (ties to even) of x, as a float; |x| >= 65520 -> inf."""
+    return float(lib().orc_round_fp16(float(x)))
+
+
+def potrf_mp_emul(A, nb: int, pmap) -> tuple[np.ndarray, int]:
+    """Emulated mixed-precision tile Cholesky of the scaled matrix A (Sec. IV-B): every tile
+    stored in its precision of pmap (nt x nt), FP32 accumulation in reduced-precision updates.
+    Returns (L_s with zeros above the diagonal, info)."""
+    A = np.array(A, dtype=np.float64, order="F", copy=True)
+    n = A.shape[0]
+    nt = (n + nb - 1) // nb
+    pm = np.ascontiguousarray(np.asarray(pmap, dtype=np.uint8).reshape(nt, nt))
+    info = lib().orc_potrf_mp_emul(A, n, n, nb, pm)
+    return A, int(info)
+
+
+def trmm_mp_emul(Ls, nb: int, s: float, Z, fp16_dest: bool = False) -> np.ndarray:
+    """Emulated mixed-precision TRMM of Algorithm 1: M = L_s round16(Z / s) with FP32 diagonal
+    products, FP16 off-diagonal products and FP32 sums; fp16_dest keeps the destination in FP16
+    between k-tasks as the printed algorithm does."""
+    Ls, Z = _f(Ls), _f(Z)
+    n, nsim = Z.shape
+    M = np.empty((n, nsim), order="F")
+    lib().orc_trmm_mp_emul(Ls, Ls.shape[0], n, nb, float(s), Z, n, nsim, int(bool(fp16_dest)), M, n)
+    return M

@@ -380,3 +380,156 @@ void orc_normals(uint64_t seed, uint32_t stream, int64_t n_rows, int64_t i0, int
         }
     }
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Emulated adaptive mixed precision ([MPX] Sec. IV-B, Algorithm 1, Sec. V-F).                 */
+/* IEEE 754 binary16 and binary32 rounding (round to nearest, ties to even) applied at every   */
+/* storage point of the tile algorithms, FP32 accumulation inside each reduced-precision task. */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Nearest binary16 value of x (ties to even), as a double; |x| >= 65520 gives +-inf.  Binary16
+ * has 11 significant bits, exponents -14..15 for normal numbers and the spacing 2^-24 below
+ * 2^-14 (subnormals): x is scaled by the spacing of its binade (a power of two, exact), rounded
+ * to an integer by nearbyint (ties to even in the default rounding mode) and scaled back. */
+double orc_round_fp16(double x) {
+    if (x != x || isinf(x) || x == 0.0) return x;
+    double a = fabs(x);
+    if (a >= 65520.0) return copysign(INFINITY, x);
+    int e;
+    frexp(a, &e);            /* a = f 2^e with f in [0.5, 1): the leading bit is 2^(e-1) */
+    int lead = e - 1;
+    if (lead < -14) lead = -14;
+    double q = ldexp(1.0, lead - 10);
+    return copysign(nearbyint(a / q) * q, x);
+}
+
+/* Nearest binary32 value of x (the C conversion rounds to nearest even). */
+static double round_fp32(double x) { return (double)(float)x; }
+
+/* Value of x stored in tile precision p (0 FP64, 1 FP32, 2 FP16). */
+static double store_p(double x, int p) {
+    if (p == 1) return round_fp32(x);
+    if (p == 2) return orc_round_fp16(x);
+    return x;
+}
+
+/* Emulated mixed-precision tile Cholesky of the n x n matrix A (lower triangle used; in: s^2 V,
+ * out: L_s with zeros above the diagonal), tiles of nb with the last one partial, precision map
+ * pmap (nt x nt row-major, codes 0 FP64 / 1 FP32 / 2 FP16; diagonal tiles FP64).  The steps are
+ * the right-looking tile algorithm with the precision reading of each task:
+ *   storage: every lower tile rounded to its precision;
+ *   step k: POTRF of tile (k, k) in FP64 (orc_potrf on the tile);
+ *           panel tile (i, k): L_ik = A_ik L_kk^-T by FP64 substitution, rounded once to P(i, k);
+ *           tile (j, j), j > k: A_jj -= L_jk L_jk^T in FP64;
+ *           tile (i, j), i > j > k, in P(i, j): operands rounded to P(i, j), products summed over the
+ *           tile column index in that precision's accumulator (FP64; FP32 for FP32 and FP16 tiles,
+ *           where FP16 products are exact in FP32), then A_ij = round_P(A_ij - sum).
+ * Returns 0 or the 1-based failing column. */
+int64_t orc_potrf_mp_emul(double* A, int64_t n, int64_t lda, int64_t nb, const uint8_t* pmap) {
+    int64_t nt = (n + nb - 1) / nb;
+#define P_(i, j) ((int)pmap[(size_t)(i) * (size_t)nt + (size_t)(j)])
+#define R0(i) ((i) * nb)
+#define RN(i) (((i) + 1) * nb < n ? nb : n - (i) * nb)
+    for (int64_t i = 0; i < nt; ++i)
+        for (int64_t j = 0; j < i; ++j)
+            for (int64_t c = 0; c < RN(j); ++c)
+                for (int64_t r = 0; r < RN(i); ++r) {
+                    double* a = &A[IDX(R0(i) + r, R0(j) + c, lda)];
+                    *a = store_p(*a, P_(i, j));
+                }
+    for (int64_t k = 0; k < nt; ++k) {
+        int64_t rk = RN(k);
+        double* Akk = &A[IDX(R0(k), R0(k), lda)];
+        int64_t info = orc_potrf(Akk, rk, lda);
+        if (info != 0) return R0(k) + info;
+#pragma omp parallel for schedule(dynamic)
+        for (int64_t i = k + 1; i < nt; ++i) {
+            int64_t ri = RN(i);
+            int p = P_(i, k);
+            for (int64_t r = 0; r < ri; ++r) {
+                /* row r of L_ik: x L_kk^T = a, forward substitution over the columns */
+                double x[4096];
+                for (int64_t c = 0; c < rk; ++c) {
+                    double sacc = A[IDX(R0(i) + r, R0(k) + c, lda)];
+                    for (int64_t m = 0; m < c; ++m) sacc -= x[m] * Akk[IDX(c, m, lda)];
+                    x[c] = sacc / Akk[IDX(c, c, lda)];
+                }
+                for (int64_t c = 0; c < rk; ++c) A[IDX(R0(i) + r, R0(k) + c, lda)] = store_p(x[c], p);
+            }
+        }
+        int64_t m_tiles = nt - k - 1;
+#pragma omp parallel for schedule(dynamic)
+        for (int64_t q = 0; q < m_tiles * m_tiles; ++q) {
+            int64_t j = k + 1 + q / m_tiles, i = k + 1 + q % m_tiles;
+            if (i < j) continue;
+            int64_t ri = RN(i), rj = RN(j);
+            int p = (i == j) ? 0 : P_(i, j);
+            for (int64_t c = 0; c < rj; ++c)
+                for (int64_t r = (i == j ? c : 0); r < ri; ++r) {
+                    double* a = &A[IDX(R0(i) + r, R0(j) + c, lda)];
+                    if (p == 0) {
+                        double sacc = 0.0;
+                        for (int64_t m = 0; m < rk; ++m)
+                            sacc += A[IDX(R0(i) + r, R0(k) + m, lda)] * A[IDX(R0(j) + c, R0(k) + m, lda)];
+                        *a = *a - sacc;
+                    } else {
+                        float facc = 0.0f;
+                        for (int64_t m = 0; m < rk; ++m) {
+                            float x = (float)store_p(A[IDX(R0(i) + r, R0(k) + m, lda)], p);
+                            float y = (float)store_p(A[IDX(R0(j) + c, R0(k) + m, lda)], p);
+                            facc += x * y;
+                        }
+                        *a = store_p((double)((float)*a - facc), p);
+                    }
+                }
+        }
+    }
+    for (int64_t j = 1; j < n; ++j)
+        for (int64_t i = 0; i < j; ++i) A[IDX(i, j, lda)] = 0.0;
+    return 0;
+#undef P_
+#undef R0
+#undef RN
+}
+
+/* Emulated mixed-precision TRMM M = L_s B, B = round16(Z / s) ([MPX] Algorithm 1 with AMP = 1):
+ * Ls holds the stored factor values (n x n lower), tiles of nb, map pmap as above.  Row tile i of
+ * column j:
+ *   diagonal: FP32 product of cast32(L_ii) and cast32(B_i) (FP32 products and sums);
+ *   off-diagonal tile k < i: FP16 operands cast16(L_ik) and B_k, products exact in FP32, summed in
+ *   FP32 over the tile's columns.
+ * fp16_dest = 1 (Algorithm 1 as printed, FP16 destination storage): the diagonal product is
+ * rounded to FP16, then for k = 0 .. i-1 the running value enters an FP32 sum with tile k's
+ * products and the result is rounded to FP16.  fp16_dest = 0: one FP32 sum of all off-diagonal
+ * products of the row, added in FP64 to the FP32 diagonal product.  M is FP64. */
+void orc_trmm_mp_emul(const double* Ls, int64_t ldl, int64_t n, int64_t nb, double s, const double* Z,
+                      int64_t ldz, int64_t nsim, int fp16_dest, double* M, int64_t ldm) {
+    int64_t nt = (n + nb - 1) / nb;
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < nsim; ++j) {
+        double* b = (double*)malloc(sizeof(double) * (size_t)n);
+        for (int64_t i = 0; i < n; ++i) b[i] = orc_round_fp16(Z[IDX(i, j, ldz)] / s);
+        for (int64_t ti = 0; ti < nt; ++ti) {
+            int64_t r0 = ti * nb, r1 = (ti + 1) * nb < n ? (ti + 1) * nb : n;
+            for (int64_t r = r0; r < r1; ++r) {
+                float d = 0.0f;
+                for (int64_t m = r0; m <= r; ++m) d += (float)Ls[IDX(r, m, ldl)] * (float)b[m];
+                if (fp16_dest) {
+                    float dest = (float)orc_round_fp16((double)d);
+                    for (int64_t tk = 0; tk < ti; ++tk) {
+                        float acc = dest;
+                        for (int64_t m = tk * nb; m < (tk + 1) * nb; ++m)
+                            acc += (float)orc_round_fp16(Ls[IDX(r, m, ldl)]) * (float)b[m];
+                        dest = (float)orc_round_fp16((double)acc);
+                    }
+                    M[IDX(r, j, ldm)] = (double)dest;
+                } else {
+                    float acc = 0.0f;
+                    for (int64_t m = 0; m < r0; ++m) acc += (float)orc_round_fp16(Ls[IDX(r, m, ldl)]) * (float)b[m];
+                    M[IDX(r, j, ldm)] = (double)d + (double)acc;
+                }
+            }
+        }
+        free(b);
+    }
+}

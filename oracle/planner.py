@@ -14,7 +14,9 @@ Readings where the pages leave a step open:
   * Eq. 11 is read as max(rho1, rho2) < 1e-4 / eps_FP16 with eps_FP16 = 2^-10 (the extraction
     prints the fraction's numerator first, as it does for Eq. 10);
   * Eq. 10 with no FP16 tiles passes vacuously; with a non-positive FP16 minimum it fails;
-  * Eq. 12 with no reduced-precision tile present gives u_s = 65504 and s = 65503.
+  * Eq. 12 with no reduced-precision tile present gives u_s = 65504 and s = 65503;
+  * the FP16 cast of L_s in Algorithm 1 adds u_L = 65504 / sqrt(max_i V_ii) to the minimum that
+    defines u_s (|(L_s)_ij| <= s sqrt(V_ii)); it binds only when max_i V_ii > 1.
 ||V||_F^2 is summed over tiles in row-packed order t = i(i+1)/2 + j, off-diagonal tiles twice.
 
 Precision codes: 0 = FP64, 1 = FP32, 2 = FP16 (255 above the diagonal).
@@ -57,6 +59,7 @@ class PlanResult:
     tiles: tuple                # (n FP64, n FP32, n FP16) over the lower triangle
     tol: float = 0.0            # tolerance of this map (the final one in automatic mode)
     reductions: int = 0         # automatic mode: number of 0.9 reductions
+    u_factor: float = float("inf")   # bound on s from the FP16 cast of L_s
 
 
 def plan_auto(stats: np.ndarray, nt: int, allow_fp16: bool = True, nt_rule: bool = True) -> PlanResult:
@@ -134,7 +137,12 @@ def plan(stats: np.ndarray, nt: int, tol: float, amp: int = 1, allow_fp16: bool 
         l_b = max(l_b, lf)
         l_sub = max(l_sub, lsf)
         u_min = min(u_min, uf)
-    u_s = min(65504.0, u_min)
+    # Algorithm 1 casts the scaled factor L_s to FP16 and every entry obeys |(L_s)_ij| <= s sqrt(V_ii)
+    # (row i of L_s has squared norm s^2 V_ii), so s <= x_max,FP16 / sqrt(max_i V_ii) keeps it finite.
+    vmax_diag = max(float(st(i, i)[2]) for i in range(nt))
+    u_factor = X_MAX[FP16] / math.sqrt(vmax_diag) if vmax_diag > 0.0 else float("inf")
+    u_s = min(65504.0, u_min, u_factor)
     s_cand = math.floor(u_s) - 1.0
     s = s_cand if s_cand > 1.0 else 1.0
-    return PlanResult(pmap, s, frob, l_b, u_s, l_b > u_s, l_sub, r_hp, rho1, rho2, eq10, eq11, counts, tol)
+    return PlanResult(pmap, s, frob, l_b, u_s, l_b > u_s, l_sub, r_hp, rho1, rho2, eq10, eq11, counts, tol,
+                      u_factor=u_factor)

@@ -56,8 +56,13 @@ def test_region_coverage(setup, amp):
     ctx = g.Context(0)
     params = {"kind": w.kind, "sigma2": w.sigma2, "range": w.beta, "nu": w.nu}
     n = N_P + N_O
+    # mixed: tol 1e-8 with the unscaled rule, so that the joint factor holds FP32 tiles (on this
+    # 8 x 8 tile shape the tile-count-scaled rule keeps every tile FP64)
     A = g.cov_gen(ctx, dev(np.r_[x, y]), n, dict(params, nugget=0.0), NB, amp=amp, tol=w.tol,
-                  diag_add=dev(diag_add))
+                  diag_add=dev(diag_add), nt_rule=not amp)
+    if amp:
+        assert A.diag["tiles"][1] + A.diag["tiles"][2] > 0, "the mixed case must hold reduced-precision tiles"
+        print(f"mixed joint factor: tiles {A.diag['tiles']}", flush=True)
     assert g.potrf_mp(ctx, A) == 0
     loc_o, loc_p = dev(np.r_[xo, yo]), dev(np.r_[xp, yp])
     inner = outer = joint = 0

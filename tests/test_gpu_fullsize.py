@@ -120,6 +120,54 @@ def test_mixed_precision_workload_fullsize(ctx):
     assert mism <= 2e-2
 
 
+def test_mixed_precision_workload_fullsize_tol1e8(ctx):
+    # N = 40,000, tile 512, tol 1e-8: FP64 and FP32 tiles in the factor
+    ef, em, mism = _unconditional_fullsize(ctx, "unif40k_tol1e-8", 2048, 5e-3, 1e-2,
+                                           [0, 511, 512, 20000, 39999])
+    assert mism <= 2e-2
+
+
+@pytest.mark.parametrize("beta", [0.03, 0.1, 0.3])
+def test_unif10k_configured_size(ctx, beta):
+    """N = 10,000 uniform locations, Matern 3/2, tile 320, tol 1e-9 (default rule), 500 seeded
+    simulations: the whole factor against the oracle's, M against L Z with the oracle's seeded
+    normals, and the exceedance counts."""
+    w = syn.workload(f"unif10k_b{beta}")
+    x, y = w.locations()
+    params = {"kind": w.kind, "sigma2": w.sigma2, "range": w.beta, "nu": w.nu, "nugget": w.nugget}
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), w.n, params, w.nb, amp=w.amp, tol=w.tol)
+    info = A.info()
+    r = oracle.plan(A.stats(), info["nt"], w.tol, amp=w.amp)
+    low = np.tril_indices(info["nt"])
+    assert np.array_equal(info["map"][low], r.pmap[low]) and info["s"] == r.s
+    tiles = A.diag["tiles"]
+    reduced = tiles[1] + tiles[2] > 0
+    if beta < 0.3:
+        assert reduced, "the weak and medium correlation levels must hold reduced-precision tiles"
+    assert g.potrf_mp(ctx, A) == 0
+    L = A.to_dense().cpu().numpy()
+    M, _ = g.trmm_sim(ctx, A, w.nsim, seed=w.seed_sim)
+    out = g.excursion_regions(ctx, M, w.n, 0, w.nsim, w.u)
+    Mg = M.cpu().numpy()
+    cg = out["counts"].cpu().numpy()
+    A.close()
+    V = oracle.cov_matrix(x, y, w.kind, w.sigma2, w.beta, w.nu, nugget=w.nugget)
+    Lo, io = oracle.potrf(V)
+    assert io == 0
+    del V
+    ef = rel(L, Lo)
+    del L
+    Mo = oracle.trmm(Lo, oracle.normals(w.seed_sim, 0, w.n, w.nsim))
+    em = rel(Mg, Mo)
+    co = oracle.scan(Mo, w.u)["counts"]
+    mism = np.abs(cg - co).sum() / (w.n * w.nsim)
+    log(f"unif10k range {beta}: map {tiles} s {r.s} factor {ef:.3e} M {em:.3e} count mismatch {mism:.2e}")
+    assert ef <= (5e-3 if reduced else 1e-10)
+    assert em <= 1e-2
+    assert mism <= 1e-2
+    assert int(out["counts"].sum()) == int(out["sizes"].sum())
+
+
 def test_grid_workload_fullsize_seeded_counts(ctx):
     # the 40 x 40 grid, all-FP64, seeded normals: counts equal the oracle's except near-ties
     w = syn.workload("grid1600_fp64")

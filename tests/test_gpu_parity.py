@@ -4,6 +4,8 @@ Tolerances: all-FP64 path relative Frobenius 1e-10 and bit-exact integer exceeda
 mixed-precision path 5e-3 for the factor and 1e-2 for simulated fields (relative Frobenius).
 Sizes span several tiles with a ragged last tile.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -364,7 +366,8 @@ def test_small_and_ragged_fp64(ctx, n, nb, nsim):
 def test_single_tile_mixed_precision_simulation(ctx):
     """One tile (no off-diagonal work): the mixed-precision product is the FP32 diagonal alone,
     applied to B = Z / s rounded to FP16, with the scale s of Eq. 12 (no reduced-precision tile:
-    s = 65503).  This is the per-step product path (there are no row panels)."""
+    u_s = min(65504, 65504 / sqrt(max V_ii)) with max V_ii = 1 + 1e-4, so s = 65499).  This is the
+    per-step product path (there are no row panels)."""
     n, nb, nsim = 150, 160, 64
     x, y, params = setup_case(n, nb, 0.5, 0.1, 9)
     A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=1e-8)
@@ -376,7 +379,7 @@ def test_single_tile_mixed_precision_simulation(ctx):
     Mo = oracle.trmm(Lo, Z)
     assert rel(M.cpu().numpy(), Mo) <= 1e-2
     s = A.diag["s"]
-    assert s == 65503.0
+    assert s == math.floor(65504.0 / math.sqrt(1.0 + 1e-4)) - 1.0 == 65499.0
     assert d["norm_B"] == pytest.approx(np.linalg.norm(Z / s), rel=1e-12)   # of Z / s before rounding
     A.close()
 
