@@ -14,7 +14,7 @@ Phase times come from HIP events on the library's stream; the dominant kernel's 
 the library's own per-launch events.  The CPU baseline times the oracle on a bounded leading
 block of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--trmm-sweep | --krige]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--trmm-sweep | --krige | --study]
 """
 import argparse
 import dataclasses
@@ -247,6 +247,120 @@ def krige_bench(args):
     }), flush=True)
 
 
+STUDY_RANGES = (("weak", 0.033), ("medium", 0.1), ("strong", 0.234))
+# (label, amp, fixedacc, FP16 destination between TRMM k-tasks)
+STUDY_LEVELS = (("DP", 0, 0.0, False), ("1e-8", 1, 1e-8, False), ("1e-6", 1, 1e-6, False), ("1e-4", 1, 1e-4, False),
+                ("1e-4 fp16-dest", 1, 1e-4, True))
+
+
+def study(args):
+    """The pages' simulation study on one GPU ("Mixed-Precision GPU Acceleration for Confidence
+    Regions of Spatial Excursion Sets", Sec. VI-B; Fig. 3 coverage, the DP-vs-fixedacc = 1e-4 cell
+    differences, Fig. 5 FP16 tile shares).  Per correlation level (range 0.033 / 0.1 / 0.234):
+    3,200 uniform observation locations and a 120 x 120 prediction grid (n = 17,600, prediction
+    rows first, each block in Morton order), exponential covariance (Matern 1/2, sigma^2 = 1),
+    trend (0, 15, 10) on (1, x, y), u = 10, tau^2 = 0.01 on the observation block, 80,000
+    conditional simulations, level 0.9.  Every replicate draws the truth (Z_p, Y_o) = X b + L_V eta
+    from the library's FP64 factor of the joint covariance, kriges, and for every precision level
+    simulates (same seed), conditions and calibrates; coverage is the share of replicates whose
+    C_in lies inside the true excursion set (inner) and whose true set lies inside C_out (outer).
+    Levels: all-FP64, fixedacc 1e-8, 1e-6, 1e-4, and 1e-4 with the FP16 destination of
+    Algorithm 1.  Tile 512 (the FP16-destination path needs a multiple of 128).  The FP16 shares of
+    Fig. 5 come from the automatic tolerance selection on the pages' 34 x 34 tile grid (tile 528)."""
+    import numpy as np
+    import torch
+
+    import gp_conditional_simulation_amd as g
+    import gpex_synth as syn
+
+    dev = torch.device("cuda:0")
+    f64 = lambda a: torch.tensor(np.ascontiguousarray(a), dtype=torch.float64, device=dev)   # noqa: E731
+    reps, nsim, nb, u, level, tau2 = args.study_reps, args.study_nsim, 512, 10.0, 0.9, 0.01
+    ranges = [rg for rg in STUDY_RANGES if rg[0] in args.study_ranges.split(",")]
+    xp, yp = syn.grid_centres(120)
+    xo, yo = syn.uniform_locations(3200, 3005)
+    xp, yp, _ = syn.ordered_locations(xp, yp)
+    xo, yo, _ = syn.ordered_locations(xo, yo)
+    n_p, n_o = len(xp), len(xo)
+    n = n_p + n_o
+    x, y = np.r_[xp, xo], np.r_[yp, yo]
+    mean = f64(syn.trend_mean(x, y, (0.0, 15.0, 10.0)))
+    diag_add = f64(np.r_[np.zeros(n_p), np.full(n_o, tau2)])
+    loc, loc_o, loc_p = f64(np.r_[x, y]), f64(np.r_[xo, yo]), f64(np.r_[xp, yp])
+    ctx = g.Context(0)
+    out = {"design": {"n_p": n_p, "n_o": n_o, "nsim": nsim, "reps": reps, "u": u, "level": level, "tau2": tau2,
+                      "nb": nb, "trend": [0.0, 15.0, 10.0], "nu": 0.5}, "ranges": []}
+    t_start = time.time()
+    M = g.colmajor(n, nsim, ctx)
+    for name, beta in ranges:
+        params = {"kind": 0, "sigma2": 1.0, "range": beta, "nu": 0.5, "nugget": 0.0}
+        # Fig. 5: FP16 share after the automatic tolerance selection, on 34 x 34 tiles
+        A = g.cov_gen(ctx, loc, n, params, 528, amp=1, auto_tol=True, diag_add=diag_add)
+        auto = {"nt": A.info()["nt"], "tiles_fp64_fp32_fp16": A.diag["tiles"], "tol": A.diag["tol"],
+                "reductions": A.diag["tol_reductions"],
+                "fp16_share": A.diag["tiles"][2] / sum(A.diag["tiles"])}
+        A.close()
+        # truths: the FP64 factor of the joint covariance times seeded N(0, 1) columns
+        AV = g.cov_gen(ctx, loc, n, params, nb, amp=0, diag_add=diag_add)
+        if g.potrf_mp(ctx, AV) != 0:
+            raise RuntimeError("joint covariance not positive definite")
+        T, _ = g.trmm_sim(ctx, AV, reps, seed=777000 + int(beta * 1000), want_diag=False)
+        T = T + mean[:, None]
+        AV.close()
+        facs, rows = {}, []
+        for label, amp, tol, emu in STUDY_LEVELS:
+            A = g.cov_gen(ctx, loc, n, params, nb, amp=amp, tol=tol, diag_add=diag_add, fp16_dest=emu)
+            info = g.potrf_mp(ctx, A)
+            rec = {"level": label, "tiles_fp64_fp32_fp16": A.diag["tiles"], "s": A.diag["s"],
+                   "eq10_pass": A.diag["eq10_pass"], "eq11_pass": A.diag["eq11_pass"], "potrf_info": info,
+                   "inner": 0, "outer": 0, "joint": 0, "diff_in": 0.0, "diff_out": 0.0}
+            if info != 0:
+                A.close()
+                rec["skipped"] = "factorization lost positive definiteness"
+            else:
+                facs[label] = A
+            rows.append(rec)
+        live = [r for r in rows if "skipped" not in r]
+        t0 = time.time()
+        for r in range(reps):
+            field = T[:, r]
+            z_p, y_o = field[:n_p], field[n_p:].contiguous()
+            truth = z_p >= u
+            W, zhat, v, info = g.krige(ctx, loc_o, n_o, loc_p, n_p, y_o, 3, params, tau2, nb)
+            if info != 0:
+                raise RuntimeError("kriging failed")
+            ref = None
+            for rec in live:
+                g.trmm_sim(ctx, facs[rec["level"]], nsim, seed=4000 + r, M=M, want_diag=False)
+                o = g.excursion_regions(ctx, M, n_p, n_o, nsim, u, level, W=W, y_o=y_o, zhat=zhat, v=v)
+                if o["status"] != 0:
+                    raise RuntimeError(f"calibration failed: status {o['status']}")
+                cin, cout = o["cin"].bool(), o["cout"].bool()
+                ok_in = not bool((cin & ~truth).any())
+                ok_out = not bool((truth & ~cout).any())
+                rec["inner"] += ok_in
+                rec["outer"] += ok_out
+                rec["joint"] += ok_in and ok_out
+                if ref is None:
+                    ref = (cin, cout)
+                rec["diff_in"] += float((cin != ref[0]).double().mean())
+                rec["diff_out"] += float((cout != ref[1]).double().mean())
+            if (r + 1) % 25 == 0:
+                log(f"{name} replicate {r + 1}/{reps}: " + ", ".join(
+                    f"{rec['level']} {rec['inner'] / (r + 1):.3f}/{rec['outer'] / (r + 1):.3f}" for rec in live) +
+                    f"  ({time.time() - t0:.0f} s)")
+        for rec in rows:
+            for k in ("inner", "outer", "joint", "diff_in", "diff_out"):
+                rec[k] = rec[k] / reps
+        for A in facs.values():
+            A.close()
+        out["ranges"].append({"correlation": name, "range": beta, "auto_tolerance_plan": auto, "levels": rows,
+                              "seconds": round(time.time() - t0, 1)})
+    out["seconds"] = round(time.time() - t_start, 1)
+    out["binomial_se_at_0.9"] = float(np.sqrt(0.09 / reps))
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -262,6 +376,11 @@ def main():
                     help="TRMM throughput against N at three correlation levels instead of the step benchmark")
     ap.add_argument("--krige", action="store_true",
                     help="the kriging workload's conditional path instead of the step benchmark")
+    ap.add_argument("--study", action="store_true",
+                    help="the pages' simulation study (coverage and region differences per tolerance level)")
+    ap.add_argument("--study-reps", type=int, default=200)
+    ap.add_argument("--study-nsim", type=int, default=80000)
+    ap.add_argument("--study-ranges", default="weak,medium,strong")
     ap.add_argument("--sweep-nsim", type=int, default=2048)
     ap.add_argument("--sweep-max-n", type=int, default=131072)
     args = ap.parse_args()
@@ -274,6 +393,9 @@ def main():
         return
     if args.krige:
         krige_bench(args)
+        return
+    if args.study:
+        study(args)
         return
 
     import numpy as np
