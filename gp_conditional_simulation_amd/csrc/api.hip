@@ -1,9 +1,39 @@
 // Context, error reporting, allocation and tiled-matrix lifecycle of libgpex.
 #include <cstring>
+#include <mutex>
 
 #include "common.h"
 
 namespace gpex {
+
+// Scratch memory of the allocation-free entry points: one fixed array per GPU, held from the
+// library's load until the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address is looked up once per device (gpex_ctx_create, with the
+// device current) and only that address is handed to kernels.  Every call on a GPU shares that
+// GPU's array, so such calls that overlap on one GPU race.
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+constexpr int MAX_DEVICES = 64;
+static void* g_scratch[MAX_DEVICES] = {};
+static std::mutex g_scratch_mu;
+
+static int scratch_lookup(int device) {
+    if (device >= MAX_DEVICES) return GPEX_OK;   // such a device simply has no scratch
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch[device]) return GPEX_OK;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return GPEX_ERR_HIP;
+    }
+    g_scratch[device] = p;
+    return GPEX_OK;
+}
+
+void* scratch_ptr(int device) {
+    if (device < 0 || device >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    return g_scratch[device];
+}
 
 int set_err(gpex_ctx_t ctx, int code, const std::string& msg) {
     if (ctx) ctx->err = msg;
@@ -87,6 +117,7 @@ extern "C" int gpex_ctx_create(int device, void* hip_stream, void* (*alloc)(size
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || device < 0 || device >= ndev) return GPEX_ERR_ARG;
     if (hipSetDevice(device) != hipSuccess) return GPEX_ERR_HIP;
+    if (scratch_lookup(device) != GPEX_OK) return GPEX_ERR_HIP;
     auto* c = new gpex_ctx_s();
     c->device = device;
     c->stream = static_cast<hipStream_t>(hip_stream);

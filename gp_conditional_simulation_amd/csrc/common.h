@@ -126,6 +126,10 @@ struct Carve {
 };
 // A timing-disabled event from the context's pool (index i, created on first use).
 int ctx_event(gpex_ctx_t ctx, size_t i, hipEvent_t* out);
+// Device address of the fixed scratch array of the allocation-free entry points on `device`
+// (NULL before a context was created on it).
+constexpr size_t SCRATCH_BYTES = size_t(32) << 20;
+void* scratch_ptr(int device);
 
 // ---- batched mixed-precision GEMM engine (gemm.hip) ---------------------------------------
 // One task: C (M x N) = alpha * op(A) * op(B) + beta * C.  op(A) is M x K, op(B) is K x N.

@@ -231,6 +231,12 @@ static int scan_groups(int64_t np, int64_t nsim) {
     return (int)(G < 1 ? 1 : G);
 }
 
+// S (n x m, leading dim n) += g 1^T
+__global__ void k_add_rows(double* S, int64_t n, int64_t m, const double* g) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx < n * m) S[idx] += g[idx % n];
+}
+
 __global__ void k_fill_i64(int64_t* a, int64_t n, int64_t v) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) a[i] = v;
@@ -461,10 +467,12 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     return GPEX_OK;
 }
 
-// Device temporaries of one gpex_excursion_regions call (S and the residual only when n_o > 0).
+// Device temporaries of one gpex_excursion_regions call (S and the residual only when n_o > 0;
+// gvec instead of the residual in the residual-free conditioning of the allocation-free variant).
 struct ScanMem {
     double *S, *R, *t, *pp, *pq, *psi, *phi;
     int* sp;
+    double* gvec;
 };
 
 static void scan_carve(Carve& cv, int64_t n_p, int64_t n_o, int64_t nsim, bool need_S, size_t piece[8]) {
@@ -519,7 +527,18 @@ static int excursion_run(gpex_ctx_t ctx, const ScanMem& m, const double* d_M, in
     const bool regions = d_zhat != nullptr;
     const double* S = d_M;
     int64_t lds = ldm;
-    if (n_o > 0) {
+    if (n_o > 0 && m.gvec) {
+        // residual-free Eq. 7 (no n_o x nsim temporary): S = M_p - W^T M_o, then S += (W^T y_o) 1^T
+        GPEX_TRY(copy2d(ctx, s, d_M, DT_F64, ldm, d_S, DT_F64, n_p, n_p, nsim, 1.0));
+        GPEX_TRY(gemm1(ctx, DT_F64, d_W, DT_F64, 1, n_o, d_M + n_p, DT_F64, 0, ldm, d_S, DT_F64, n_p, (int)n_p,
+                       (int)nsim, (int)n_o, -1.0, 1.0));
+        GPEX_TRY(gemm1(ctx, DT_F64, d_W, DT_F64, 1, n_o, d_y_o, DT_F64, 0, n_o, m.gvec, DT_F64, n_p, (int)n_p, 1,
+                       (int)n_o, 1.0, 0.0));
+        hipLaunchKernelGGL(k_add_rows, dim3(blocks(n_p * nsim)), dim3(256), 0, s, d_S, n_p, nsim, m.gvec);
+        GPEX_HIP(ctx, hipGetLastError());
+        S = d_S;
+        lds = n_p;
+    } else if (n_o > 0) {
         double* Sbuf = d_S ? d_S : m.S;
         GPEX_TRY(copy2d(ctx, s, d_M, DT_F64, ldm, Sbuf, DT_F64, n_p, n_p, nsim, 1.0));
         hipLaunchKernelGGL(k_residual, dim3(blocks(n_o * nsim)), dim3(256), 0, s, d_M, ldm, n_p, n_o, nsim, d_y_o, m.R);
@@ -599,3 +618,38 @@ extern "C" int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t
                          d_counts, d_sizes, h_psi, h_phi, d_cin, d_cout, d_S, st);
 }
 
+// Allocation-free variant: the temporaries live in the library's fixed per-GPU scratch array and
+// the conditioning runs without the n_o x nsim residual.
+extern "C" int gpex_excursion_regions_noalloc(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p,
+                                              int64_t n_o, int64_t nsim, const double* d_W, const double* d_y_o,
+                                              const double* d_zhat, const double* d_v, double u, double level_c,
+                                              int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
+                                              uint8_t* d_cin, uint8_t* d_cout, double* d_S,
+                                              gpex_region_stats* st) {
+    if (!ctx) return GPEX_ERR_ARG;
+    GPEX_TRY(excursion_check(ctx, d_M, ldm, n_p, n_o, nsim, d_W, d_y_o, d_zhat, d_v, level_c, d_counts, d_sizes,
+                             h_psi, h_phi, d_cin, d_cout));
+    if (n_o > 0 && !d_S)
+        return set_err(ctx, GPEX_ERR_ARG, "gpex_excursion_regions_noalloc: d_S is needed when n_o > 0");
+    GPEX_HIP(ctx, hipSetDevice(ctx->device));
+    void* base = scratch_ptr(ctx->device);
+    if (!base) return set_err(ctx, GPEX_ERR_STATE, "gpex_excursion_regions_noalloc: no scratch on this device");
+    Carve cv;
+    size_t piece[8];
+    scan_carve(cv, n_p, 0, nsim, false, piece);   // t, partials, psi, phi
+    const size_t p_g = cv.add(n_o > 0 ? sizeof(double) * n_p : 0);
+    if (cv.total > SCRATCH_BYTES)
+        return set_err(ctx, GPEX_ERR_ARG, "gpex_excursion_regions_noalloc: needs " + std::to_string(cv.total) +
+                                              " bytes of scratch, the maximum is " + std::to_string(SCRATCH_BYTES));
+    ScanMem m = scan_mem(cv, base, piece);
+    m.S = nullptr;
+    m.R = nullptr;
+    m.gvec = n_o > 0 ? cv.get<double>(base, p_g) : nullptr;
+    // the conditioning product stays on the context stream (no side stream to create)
+    const bool serial = ctx->serial;
+    ctx->serial = true;
+    const int r = excursion_run(ctx, m, d_M, ldm, n_p, n_o, nsim, d_W, d_y_o, d_zhat, d_v, u, level_c, d_counts,
+                                d_sizes, h_psi, h_phi, d_cin, d_cout, d_S, st);
+    ctx->serial = serial;
+    return r;
+}

@@ -273,6 +273,25 @@ int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64
                            int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
                            uint8_t* d_cin, uint8_t* d_cout, double* d_S, gpex_region_stats* st);
 
+/* Allocation-free variant of gpex_excursion_regions, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, results and return codes, with these differences:
+ *   - the temporaries (t, per-group partials, psi/phi, and W^T y_o when n_o > 0) live in one fixed
+ *     32 MiB device array per GPU that the library holds from its load until the process ends;
+ *     a call whose temporaries need more returns GPEX_ERR_ARG (about 8 n_p + 20 G nsim + 16 nsim
+ *     bytes, with G <= 256 row groups: n_p = 10^6 with nsim = 2,000 fits);
+ *   - d_S is required when n_o > 0, and Eq. 7 is evaluated without the n_o x nsim residual:
+ *     S = M_p - W^T M_o, then S += (W^T y_o) 1^T (the same S up to rounding order);
+ *   - the conditioning product runs on the context stream only (no side stream is created).
+ * It calls no hipMalloc / hipFree and no allocating library routine.  Every call on one GPU
+ * shares that GPU's array, and the array keeps the last call's contents: calls that overlap on
+ * one GPU (several contexts or threads) race, so callers serialise them. */
+int gpex_excursion_regions_noalloc(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p,
+                                   int64_t n_o, int64_t nsim, const double* d_W, const double* d_y_o,
+                                   const double* d_zhat, const double* d_v, double u, double level_c,
+                                   int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
+                                   uint8_t* d_cin, uint8_t* d_cout, double* d_S, gpex_region_stats* st);
+
 /* ---- timing support ------------------------------------------------------------------------ */
 /* Per-phase device time of the last gpex_potrf_mp / gpex_trmm_sim on ctx, measured with HIP
  * events recorded around the launches on the streams they run on (enable with
