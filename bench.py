@@ -370,6 +370,8 @@ def main():
     ap.add_argument("--nb", type=int, default=0, help="tile size override for --workload / --krige (0: the recipe's)")
     ap.add_argument("--cpu-rows", type=int, default=10240)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mp", action="store_true", help="skip the mixed-precision N = 100k workloads")
+    ap.add_argument("--mp-steps", type=int, default=2)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (HBM counter calibration)")
     ap.add_argument("--trmm-sweep", action="store_true",
@@ -533,10 +535,78 @@ def main():
                                if trmm_rows_ms else None},
         "counts_sum": last["counts_sum"],
     }
+    if not args.no_mp and args.workload == "unif100k_tol1e-8":
+        res["mixed_precision_workloads"] = [mp_workload(args, name, ctx, loc, M) for name in MP_WORKLOADS]
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_rows)
     print(json.dumps(res), flush=True)
+
+
+# Same locations and tolerance as the headline workload at medium and weak correlation, where the
+# precision map holds FP32 (and FP16) tiles; measured after the headline, reported beside it.
+MP_WORKLOADS = ("unif100k_b0.1_tol1e-8", "unif100k_b0.03_tol1e-8")
+
+
+def mp_workload(args, name, ctx, loc, M):
+    """Factorization + simulation product of a mixed-precision N = 100k workload: args.mp_steps
+    measured steps after one warm-up, medians; per-precision trailing-update rates over their
+    launches (flops on true tile sizes / summed launch time, and over the busy time)."""
+    import torch
+
+    import gp_conditional_simulation_amd as g
+    import gpex_synth as syn
+
+    w = syn.workload(name)
+    params = {"kind": w.kind, "sigma2": w.sigma2, "range": w.beta, "nu": w.nu, "nugget": w.nugget}
+    recs = []
+    for i in range(1 + args.mp_steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        A = g.cov_gen(ctx, loc, w.n, params, w.nb, amp=w.amp, tol=w.tol)
+        ev[0].record()
+        info = g.potrf_mp(ctx, A)
+        if info != 0:
+            raise RuntimeError(f"{name}: factorisation failed at column {info}")
+        ev[1].record()
+        g.trmm_sim(ctx, A, w.nsim, seed=w.seed_sim, M=M, want_diag=False)
+        ev[2].record()
+        torch.cuda.synchronize()
+        r = {"potrf": ev[0].elapsed_time(ev[1]), "trmm": ev[1].elapsed_time(ev[2]), "lib": ctx.timings(),
+             "diag": dict(A.diag), "info": A.info()}
+        A.close()
+        log(f"{name} {'warmup' if i == 0 else 'step'}: potrf {r['potrf']:.1f} ms trmm {r['trmm']:.1f} ms")
+        if i:
+            recs.append(r)
+    T_potrf = statistics.median(r["potrf"] for r in recs)
+    T_trmm = statistics.median(r["trmm"] for r in recs)
+    last = recs[-1]
+    tf = tile_flops(last["info"]["map"], last["info"]["nt"], last["info"]["nb"], w.nsim, w.amp)
+    t_ideal = sum(tf[p] / (PEAK_TF[p] * 1e12) for p in tf)
+    upd = {}
+    for p in ("fp64", "fp32", "fp16"):
+        n_l = last["lib"]["update_launches"][p]
+        if not n_l:
+            continue
+        ms = statistics.median(r["lib"]["update_ms"][p] for r in recs)
+        busy = statistics.median(r["lib"]["update_busy_ms"][p] for r in recs)
+        fl = last["lib"]["update_flops_exact"][p]
+        upd[p] = {"launches": n_l, "flops": float(f"{fl:.4e}"), "summed_launch_ms": round(ms, 2),
+                  "busy_ms": round(busy, 2), "tflops_per_launch_time": round(fl / (ms * 1e-3) / 1e12, 2),
+                  "tflops_busy": round(fl / (busy * 1e-3) / 1e12, 2),
+                  "frac_of_peak_busy": round(fl / (busy * 1e-3) / 1e12 / PEAK_TF[p], 4)}
+    d = last["diag"]
+    N = w.n
+    return {"workload": f"{w.name}: N={N}, Matern nu={w.nu} range={w.beta} nugget={w.nugget}, tile {w.nb}, "
+                        f"tol {w.tol} (tile-count-scaled rule), nsim {w.nsim}",
+            "tiles_fp64_fp32_fp16": d["tiles"], "scale_s": d["s"], "eq10_pass": d["eq10_pass"],
+            "eq11_pass": d["eq11_pass"], "steps": args.mp_steps,
+            "potrf_ms": round(T_potrf, 2), "trmm_ms": round(T_trmm, 2),
+            "value_fp64_equiv_tflops": round((N ** 3 / 3.0 + float(N) ** 2 * w.nsim) / ((T_potrf + T_trmm) * 1e-3) / 1e12,
+                                             3),
+            "precision_weighted_roofline": {"ideal_ms": round(t_ideal * 1e3, 2),
+                                            "frac": round(t_ideal / ((T_potrf + T_trmm) * 1e-3), 4),
+                                            "flops": {k: float(f"{v:.4e}") for k, v in tf.items()}},
+            "trailing_updates": upd}
 
 
 if __name__ == "__main__":

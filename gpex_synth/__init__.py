@@ -167,6 +167,12 @@ WORKLOADS = {
     # N = 100,000 uniform, Matern 3/2, range 0.3, tile 1024, tolerance 1e-8, 2,000 columns
     "unif100k_tol1e-8": Workload("unif100k_tol1e-8", n=100000, nb=1024, nu=1.5, sigma2=1.0, beta=0.3,
                                  nugget=1e-4, nsim=2000, seed_sim=2005, u=0.5, amp=1, tol=1e-8, seed_loc=1005),
+    # the same locations and tolerance at medium and weak correlation, where the map holds reduced
+    # tiles: range 0.1 gives FP64 and FP32 tiles, range 0.03 FP64, FP32 and FP16 tiles
+    **{f"unif100k_b{b}_tol1e-8": Workload(f"unif100k_b{b}_tol1e-8", n=100000, nb=1024, nu=1.5, sigma2=1.0, beta=b,
+                                          nugget=1e-4, nsim=2000, seed_sim=2005, u=0.5, amp=1, tol=1e-8,
+                                          seed_loc=1005)
+       for b in (0.1, 0.03)},
 }
 
 

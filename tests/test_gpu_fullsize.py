@@ -127,6 +127,36 @@ def test_mixed_precision_workload_fullsize_tol1e8(ctx):
     assert mism <= 2e-2
 
 
+@pytest.mark.parametrize("name", ["unif100k_b0.1_tol1e-8", "unif100k_b0.03_tol1e-8"])
+def test_mixed_precision_100k_fullsize(ctx, name):
+    """N = 100,000 at tol 1e-8 with FP32 (range 0.1) and FP16 (range 0.03) tiles in the factor: the
+    leading block (FP64 tiles there), sampled rows across the matrix (their dot products cross
+    reduced-precision tiles), M on those rows, and the precision classes of sampled reduced tiles."""
+    rows = [0, 1023, 1024, 9000, 31337, 50000, 64511, 77777, 88888, 99999]
+    ef, em, mism = _unconditional_fullsize(ctx, name, 2048, 5e-3, 1e-2, rows)
+    assert mism <= 2e-2
+    w = syn.workload(name)
+    x, y = w.locations()
+    params = {"kind": w.kind, "sigma2": w.sigma2, "range": w.beta, "nu": w.nu, "nugget": w.nugget}
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), w.n, params, w.nb, amp=w.amp, tol=w.tol)
+    tiles = A.diag["tiles"]
+    assert tiles[1] > 0 and (tiles[2] > 0 or w.beta > 0.05)
+    assert g.potrf_mp(ctx, A) == 0
+    pm, nb = A.info()["map"], w.nb
+    checked = 0
+    for p in (1, 2):
+        ij = np.argwhere(np.tril(pm == p, -1))
+        for i, j in ij[:: max(1, len(ij) // 4)][:4]:
+            t = A.block_raw(int(i) * nb, int(j) * nb, nb, nb).cpu().numpy()
+            t16 = A.block_raw(int(i) * nb, int(j) * nb, nb, nb, fp16_copy=True).cpu().numpy()
+            cast = np.float32 if p == 1 else np.float16
+            assert np.array_equal(t, t.astype(cast).astype(np.float64)), (i, j, p)
+            assert np.array_equal(t16, t.astype(np.float16).astype(np.float64)), (i, j, p)
+            checked += 1
+    log(f"  {name}: map {tiles}, {checked} reduced tiles checked for their precision class")
+    A.close()
+
+
 @pytest.mark.parametrize("beta", [0.03, 0.1, 0.3])
 def test_unif10k_configured_size(ctx, beta):
     """N = 10,000 uniform locations, Matern 3/2, tile 320, tol 1e-9 (default rule), 500 seeded
