@@ -331,6 +331,10 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
                              "FP16 factor panels"));
     // rows of tile row i that exist (the last one may be padding beyond n)
     auto rows = [&](int64_t i) { return (double)std::min<int64_t>(nb, a->n - i * nb); };
+    // FP64 tiles still hold V (the generator scaled only the reduced-precision tiles): step 0 applies
+    // s^2 to them, as alpha of their panel solves and beta of their updates; tile (0, 0) is scaled
+    // before its factorization
+    const double s2_first = a->unscaled64 ? a->s * a->s : 1.0;
 
     // Per-step task groups, built once on the host and uploaded in one copy.  A group holds the
     // tasks of one step with one compute precision and one operand-type signature (a launch runs
@@ -346,9 +350,32 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     auto sig = [](int compute, const GemmTask& g) {
         return compute * 1000 + g.ta * 100 + g.tb * 10 + g.tc;
     };
-    // workspace: panel copies (FP64-sized slots), diagonal scratch, task and copy lists
+    // Operand copies of the panel tiles for reduced-precision updates.  A trailing update computes in
+    // its output tile's precision with the operands converted to it; a panel tile that is wider than
+    // some output it feeds gets its FP32 / FP16 rounding written once by the panel solve, and those
+    // updates read the copy (the same values the kernels would convert on every load, at half or a
+    // quarter of the bytes).  Two buffers, by step parity: step k's updates (look-ahead stream) still
+    // read step k's copies while step k + 1's panel solves write theirs.
+    auto feeds = [&](int64_t i, int64_t k, int want) {   // does tile (i, k) feed an update computing in `want`?
+        for (int64_t j = k + 1; j < i; ++j)
+            if (a->prec(i, j) == want) return true;
+        for (int64_t j = i + 1; j < nt; ++j)
+            if (a->prec(j, i) == want) return true;
+        return false;
+    };
+    std::vector<uint8_t> need32((size_t)(nt * nt), 0), need16((size_t)(nt * nt), 0);
+    bool any32 = false, any16 = false;
+    for (int64_t k = 0; k + 1 < nt && a->opts.amp; ++k)
+        for (int64_t i = k + 1; i < nt; ++i) {
+            const int p = a->prec(i, k);
+            if (p == DT_F64 && feeds(i, k, DT_F32)) any32 = need32[(size_t)(i * nt + k)] = 1;
+            if (p != DT_F16 && feeds(i, k, DT_F16)) any16 = need16[(size_t)(i * nt + k)] = 1;
+        }
+    // workspace: panel copies (FP64-sized slots), diagonal scratch, operand copies, task and copy lists
     Carve cv;
     const size_t p_pws = cv.add(nt > 1 ? 8 * tile_el * (size_t)(nt - 1) : 0), p_ws = cv.add(sizeof(double) * tile_el);
+    const size_t p_c32 = cv.add(any32 ? 2 * 4 * tile_el * (size_t)(nt - 1) : 0),
+                 p_c16 = cv.add(any16 ? 2 * 2 * tile_el * (size_t)(nt - 1) : 0);
     size_t ntask = 0;
     for (int64_t k = 0; k < nt; ++k) ntask += (size_t)(nt - k - 1) + (size_t)(nt - k - 1) * (nt - k) / 2;
     const size_t p_tasks = cv.add(sizeof(GemmTask) * ntask), p_copies = cv.add(sizeof(CopyTask) * (size_t)(nt * (nt - 1) / 2));
@@ -356,6 +383,18 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     GPEX_TRY(ws_get(ctx, WS_POTRF, cv.total, &wsb, "factorization workspace"));
     uint8_t* pws = cv.get<uint8_t>(wsb, p_pws);
     double* ws = cv.get<double>(wsb, p_ws);
+    float* c32 = cv.get<float>(wsb, p_c32);
+    _Float16* c16 = cv.get<_Float16>(wsb, p_c16);
+    auto copy32 = [&](int64_t i, int64_t k) { return c32 + ((size_t)(k % 2) * (nt - 1) + (size_t)(i - k - 1)) * tile_el; };
+    auto copy16 = [&](int64_t i, int64_t k) { return c16 + ((size_t)(k % 2) * (nt - 1) + (size_t)(i - k - 1)) * tile_el; };
+    // operand (i, k) of an update computing in `want`: the copy when there is one, else the tile
+    auto operand = [&](int64_t i, int64_t k, int want, const void*& ptr, int8_t& type) {
+        const int p = a->prec(i, k);
+        if (want == DT_F32 && need32[(size_t)(i * nt + k)]) { ptr = copy32(i, k); type = DT_F32; return; }
+        if (want == DT_F16 && need16[(size_t)(i * nt + k)]) { ptr = copy16(i, k); type = DT_F16; return; }
+        ptr = a->tile(i, k);
+        type = (int8_t)p;
+    };
     GemmTask* d_tasks = cv.get<GemmTask>(wsb, p_tasks);
     CopyTask* d_copies = cv.get<CopyTask>(wsb, p_copies);
     for (int64_t k = 0; k < nt; ++k) {
@@ -376,26 +415,30 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             g.M = g.N = g.K = nb;
             g.ta = (int8_t)p; g.tb = DT_F64; g.tc = (int8_t)p;
             g.transA = 0; g.transB = 1;
-            g.alpha = 1.0; g.beta = 0.0;
+            g.alpha = (k == 0 && p == DT_F64) ? s2_first : 1.0;   // an FP64 tile still holds V
+            g.beta = 0.0;
             g.tri = TRI_B_UPPER;   // T_kk^T is upper triangular
             if (a->l16) {   // tile (i, k) lands at columns [k nb, (k+1) nb) of row panel i
                 g.C2 = a->l16_panel(i) + (size_t)k * nb;
                 g.ldc2 = i * nb;
             }
+            if (need32[(size_t)(i * nt + k)]) g.C3 = copy32(i, k);
+            if (need16[(size_t)(i * nt + k)]) g.C4 = copy16(i, k);
             panel[sig(DT_F64, g)].push_back(g);
         }
         for (int64_t j = k + 1; j < nt; ++j)
             for (int64_t i = j; i < nt; ++i) {
                 int p = (i == j) ? DT_F64 : a->prec(i, j);
                 GemmTask g{};
-                g.A = a->tile(i, k);
-                g.B = a->tile(j, k);
+                operand(i, k, p, g.A, g.ta);
+                operand(j, k, p, g.B, g.tb);
                 g.C = a->tile(i, j);
                 g.lda = g.ldb = g.ldc = nb;
                 g.M = g.N = g.K = nb;
-                g.ta = (int8_t)a->prec(i, k); g.tb = (int8_t)a->prec(j, k); g.tc = (int8_t)p;
+                g.tc = (int8_t)p;
                 g.transA = 0; g.transB = 1;
-                g.alpha = -1.0; g.beta = 1.0;
+                g.alpha = -1.0;
+                g.beta = (k == 0 && p == DT_F64) ? s2_first : 1.0;   // s^2 V - L_i0 L_j0^T for FP64 tiles
                 g.tri = (i == j) ? TRI_C_LOWER : 0;   // diagonal tiles: only the lower triangle is used
                 (j == k + 1 ? update_next : update)[sig(p, g)].push_back(g);
                 upd_flops[(size_t)p] += (i == j ? 1.0 : 2.0) * nb * (double)nb * nb;
@@ -490,6 +533,8 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         return launch_groups(k, GEMM_GENERIC, 0, s);
     };
     auto schedule = [&]() -> int {
+        if (s2_first != 1.0)
+            GPEX_TRY(copy2d(ctx, s, a->tile(0, 0), DT_F64, nb, a->tile(0, 0), DT_F64, nb, nb, nb, s2_first));
         // fork: stream B starts after everything queued so far on the context stream
         GPEX_TRY(record(evfork, s));
         GPEX_TRY(wait(sb, evfork));
@@ -565,6 +610,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         return set_err(ctx, GPEX_ERR_NOT_SPD, "gpex_potrf_mp: non-positive pivot at column " + std::to_string(fl[FLAG_INFO]));
     }
     a->factored = true;
+    a->unscaled64 = false;
     if (fl[FLAG_FP16_OVF]) {
         // a value stored in FP16 (an FP16 tile update or the FP16 copy of the factor) became +-inf
         a->diag.fp16_overflow = 1;

@@ -74,6 +74,9 @@ struct gpex_tiled_s {
     _Float16* l16_panel(int64_t i) const { return l16 + (size_t)nb * nb * (size_t)(i * (i - 1) / 2); }
     bool factored = false;
     bool failed = false;             // a factorization stopped at a non-positive pivot: tiles hold garbage
+    // FP64 tiles hold V rather than s^2 V (reduced tiles hold s^2 V): the factorization applies s^2
+    // to them in its first step
+    bool unscaled64 = false;
     gpex_prec_opts opts{};
     gpex_diag diag{};
 
@@ -147,10 +150,16 @@ struct GemmTask {
     int8_t tri;   // TRI_* flags: triangular structure the kernels may exploit (results are unchanged)
     int8_t pad1, pad2;
     double alpha, beta;
-    // Optional second output (typed kernels only): the stored result converted to FP16 and
-    // written row-major, element (row, col) at C2[col + row * ldc2].
+    // Optional second output (typed FP64-compute kernels of the generic role only, i.e. the panel
+    // solves): the stored result converted to FP16 and written row-major, element (row, col) at
+    // C2[col + row * ldc2].
     _Float16* C2;
     int64_t ldc2;
+    // Optional copies of the stored result in FP32 (C3) and FP16 (C4), column-major with leading
+    // dimension ldc (the factorization's per-step operand copies of the panel tiles; same kernels
+    // as C2).
+    float* C3;
+    _Float16* C4;
     // FP16 destination storage between k-tasks (simulation product only, whole blocks): the
     // accumulator starts from beta C, is rounded to FP16 after every kround values of k and at the
     // end of the K loop, and alpha times it is stored.  0: off.

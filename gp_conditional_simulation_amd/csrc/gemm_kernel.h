@@ -442,6 +442,8 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     // each row group's old C values are all loaded before any store, so their latencies overlap.
     bool ovf = false;
     _Float16* __restrict__ C2 = T.C2;
+    float* __restrict__ C3 = T.C3;
+    _Float16* __restrict__ C4 = T.C4;
     const bool use_beta = !EMU && T.beta != 0.0;   // EMU: the destination is in the accumulator
     auto epilogue = [&](auto out_tag) {   // out_tag: a value of the output element type
         typedef decltype(out_tag) TO;
@@ -493,10 +495,15 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
                         Cp[ci] = h;
                         sv = (double)h;
                     }
-                    if (C2) {
-                        _Float16 h2 = f64_to_f16(sv);
-                        C2[(int64_t)col + (int64_t)row * T.ldc2] = h2;
-                        if (__builtin_isinf((float)h2) && !__builtin_isinf(sv)) ovf = true;
+                    if constexpr (ROLE == GEMM_GENERIC && sizeof(CT) == 8) {
+                        // extra outputs of the panel solves (FP64 compute, generic role)
+                        if (C2) {
+                            _Float16 h2 = f64_to_f16(sv);
+                            C2[(int64_t)col + (int64_t)row * T.ldc2] = h2;
+                            if (__builtin_isinf((float)h2) && !__builtin_isinf(sv)) ovf = true;
+                        }
+                        if (C3) C3[ci] = (float)sv;            // the values the update kernels convert on load
+                        if (C4) C4[ci] = f64_to_f16(sv);
                     }
                 }
         }

@@ -151,9 +151,11 @@ const char* gpex_version(void);
  * when the caller orders them so).  The diagonal gets d_diag_add[i] when d_diag_add is not
  * NULL (this is how tau^2 enters only the observation rows), else params->nugget.
  * The matrix is cut into nb x nb tiles (NT = ceil(n / nb), last tile padded with an identity
- * diagonal and zeros).  Pass 1 computes per-tile sum of squares, minimum and maximum of the
- * unscaled entries; the host plans the precision map and s (Sec. V-D, V-E); pass 2 writes
- * s^2 V_ij of each lower tile in its precision (round to nearest even).
+ * diagonal and zeros).  One pass evaluates every entry, writes V in FP64 and computes per-tile
+ * sum of squares, minimum and maximum; the host plans the precision map and s (Sec. V-D, V-E);
+ * each reduced-precision tile is then converted in place to s^2 V_ij in its precision (round to
+ * nearest even).  FP64 tiles keep V until gpex_potrf_mp applies s^2 in its first step.  Every
+ * lower tile has an FP64-sized slot (8 nb^2 bytes), whatever its precision.
  * *out receives a library-owned tiled matrix (release with gpex_tiled_destroy).
  * diag may be NULL.  Synchronises.  Returns GPEX_OK, GPEX_WARN_CHECKS_FAILED (Eq. 10/11 failed:
  * results still produced), GPEX_WARN_FP16_OVERFLOW, or an error.
@@ -176,8 +178,9 @@ int gpex_tiled_info(gpex_tiled_t t, int64_t* n, int* nb, int64_t* nt, uint8_t* h
 /* Per-tile statistics of the unscaled matrix, 3 doubles per lower tile (sum of squares, min,
  * max) in row-packed order t = i(i+1)/2 + j.  h_stats holds 3*NT*(NT+1)/2 doubles. */
 int gpex_tiled_stats(gpex_tiled_t t, double* h_stats);
-/* Copies the stored lower tiles, converted to FP64 and unscaled (divided by s^2 before the
- * factorisation and by s after it, so a matrix reads as V and a factor as chol(V)), into the
+/* Copies the stored lower tiles, converted to FP64 and unscaled (reduced-precision tiles divided
+ * by s^2 before the factorisation, every tile by s after it, so a matrix reads as V and a factor
+ * as chol(V)), into the
  * dense n x n column-major d_out (leading dimension ld >= n); entries above the diagonal tiles
  * are set to 0.  Enqueued on ctx. */
 int gpex_tiled_to_dense(gpex_ctx_t ctx, gpex_tiled_t t, double* d_out, int64_t ld);
@@ -189,7 +192,8 @@ int gpex_tiled_to_dense(gpex_ctx_t ctx, gpex_tiled_t t, double* d_out, int64_t l
 int gpex_tiled_block(gpex_ctx_t ctx, gpex_tiled_t t, int64_t r0, int64_t c0, int64_t rows,
                      int64_t cols, double* d_out, int64_t ld);
 /* Raw values of a block, converted exactly to FP64 with no unscaling: which = 0 reads the stored
- * tiles (s^2 V before the factorisation, L_s after it; entries above the diagonal tiles read 0),
+ * tiles (before the factorisation s^2 V in reduced-precision tiles and V in FP64 tiles; L_s after
+ * it; entries above the diagonal tiles read 0),
  * which = 1 the FP16 copy of the off-diagonal factor tiles that the simulation product multiplies
  * with (Algorithm 1, cast16 of L_s; entries in diagonal tiles and above read 0; needs a factor
  * computed with amp = 1, else GPEX_ERR_STATE).  Lets a caller check that every stored value is a
