@@ -418,6 +418,8 @@ def main():
     ctx = g.Context(0)
     ctx.set_timing(True)
     M = g.colmajor(w.n, w.nsim, ctx)
+    counts_buf = torch.empty(w.n, dtype=torch.int64, device=dev)      # outputs of the scan, reused
+    sizes_buf = torch.empty(w.nsim, dtype=torch.int32, device=dev)
     if args.copy_calibration_mib:
         src = torch.ones(args.copy_calibration_mib * 2 ** 20 // 8, dtype=torch.float64, device=dev)
         dst = torch.empty_like(src)
@@ -437,7 +439,7 @@ def main():
         ev[2].record()
         _, d = g.trmm_sim(ctx, A, w.nsim, seed=w.seed_sim, M=M)
         ev[3].record()
-        out = g.excursion_regions(ctx, M, w.n, 0, w.nsim, w.u)
+        out = g.excursion_regions(ctx, M, w.n, 0, w.nsim, w.u, counts=counts_buf, sizes=sizes_buf)
         ev[4].record()
         torch.cuda.synchronize()
         ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(4)]

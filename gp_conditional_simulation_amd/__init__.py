@@ -368,15 +368,21 @@ def krige(ctx: Context, loc_o, n_o: int, loc_p, n_p: int, y_o, k_trend: int, par
 
 
 def excursion_regions(ctx: Context, M, n_p: int, n_o: int, nsim: int, u: float, level: float = 0.9, W=None,
-                      y_o=None, zhat=None, v=None, want_S=False, noalloc=False):
+                      y_o=None, zhat=None, v=None, want_S=False, noalloc=False, counts=None, sizes=None):
     """gpex_excursion_regions (gpex_excursion_regions_noalloc with noalloc=True, which needs
     want_S when n_o > 0).  M: column-major (n_p + n_o) x nsim view; W: column-major n_o x n_p view.
-    Returns dict with counts, sizes, and (with zhat) psi, phi, cin, cout, q_in, q_out, n_psi, n_phi, status."""
+    counts / sizes: optional int64 (n_p) / int32 (nsim) device outputs to reuse (the call writes
+    every entry).  Returns dict with counts, sizes, and (with zhat) psi, phi, cin, cout, q_in,
+    q_out, n_psi, n_phi, status."""
     import torch
     dev = f"cuda:{ctx.device}"
     ldm = n_p + n_o
-    counts = torch.zeros(n_p, dtype=torch.int64, device=dev)
-    sizes = torch.zeros(nsim, dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty(n_p, dtype=torch.int64, device=dev)
+    if sizes is None:
+        sizes = torch.empty(nsim, dtype=torch.int32, device=dev)
+    if counts.numel() != n_p or counts.dtype != torch.int64 or sizes.numel() != nsim or sizes.dtype != torch.int32:
+        raise ValueError("counts must be int64 of n_p entries and sizes int32 of nsim entries")
     S = torch.empty((nsim, n_p), dtype=torch.float64, device=dev) if want_S else None
     out = {"counts": counts, "sizes": sizes}
     psi = phi = cin = cout = None

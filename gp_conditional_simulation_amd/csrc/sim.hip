@@ -127,6 +127,7 @@ __global__ void k_zero_pad(int64_t n, int64_t nsim, int64_t rows_pad, int64_t co
 // ---- scan ------------------------------------------------------------------------------------
 constexpr int SROWS = 256, SCOLS = 64;   // rows of a scan tile (one per thread), columns of a block
 constexpr int SCAN_MAX_GROUPS = 256;     // row groups: per-(group, column) partials
+constexpr int SBATCH = 16;               // loads in flight per thread
 
 // Workgroup (g, cb) scans the row tiles g, g + G, g + 2G, ... of column block cb (SCOLS columns).
 // Phase 1, thread = row: reads the row's SCOLS values of S (each column read by 256 consecutive
@@ -134,8 +135,8 @@ constexpr int SCAN_MAX_GROUPS = 256;     // row groups: per-(group, column) part
 // block) and leaves the >= / <= flags of the row as two 64-bit masks in LDS.  Phase 2, thread =
 // (column, quarter of the rows): min of t over the >= rows, max over the <= rows, size of the >=
 // set, kept in registers across the group's tiles.  The quarters are folded in order at the end
-// and written as the group's partials of each column; k_scan_finish folds the groups in order.
-// Rows beyond np and columns beyond nsim carry no flags.
+// and written as the group's partials of each column; k_scan_finish folds the groups.  Rows beyond
+// np and columns beyond nsim carry no flags.
 __global__ __launch_bounds__(256) void k_scan(const double* __restrict__ S, int64_t lds, int64_t np,
                                               int64_t nsim, const double* __restrict__ t, double u, int G,
                                               unsigned long long* __restrict__ counts,
@@ -159,13 +160,18 @@ __global__ __launch_bounds__(256) void k_scan(const double* __restrict__ S, int6
         if (gr < np) {
             const double* col = S + gr + c0 * lds;
             int cnt = 0;
-#pragma unroll 16
-            for (int cc = 0; cc < SCOLS; ++cc) {
-                if (cc < ncol) {
-                    const double v = col[cc * lds];
-                    const bool a = v >= u, b = v <= u;
-                    fg |= (uint64_t)a << cc;
-                    fe |= (uint64_t)b << cc;
+            // batches of SBATCH loads issued together; a ragged block re-reads its last column
+            // (an in-bounds address) instead of branching, and masks those flags off
+            for (int cb = 0; cb < SCOLS; cb += SBATCH) {
+                double v[SBATCH];
+#pragma unroll
+                for (int k = 0; k < SBATCH; ++k) v[k] = col[(int64_t)min(cb + k, ncol - 1) * lds];
+#pragma unroll
+                for (int k = 0; k < SBATCH; ++k) {
+                    const bool ok = cb + k < ncol;
+                    const bool a = ok && v[k] >= u, b = ok && v[k] <= u;
+                    fg |= (uint64_t)a << (cb + k);
+                    fe |= (uint64_t)b << (cb + k);
                     cnt += a;
                 }
             }
@@ -204,13 +210,15 @@ __global__ __launch_bounds__(256) void k_scan(const double* __restrict__ S, int6
     }
 }
 
-// Column j: fold the G group partials in group order.
-__global__ void k_scan_finish(const double* psi_part, const double* phi_part, const int* size_part,
-                              int G, int64_t nsim, double* psi, double* phi, int* sizes) {
+// Column j: fold the G group partials (min, max and integer sums: exact in any order).
+__global__ void k_scan_finish(const double* __restrict__ psi_part, const double* __restrict__ phi_part,
+                              const int* __restrict__ size_part, int G, int64_t nsim, double* __restrict__ psi,
+                              double* __restrict__ phi, int* __restrict__ sizes) {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= nsim) return;
     double mn = INFINITY, mx = -INFINITY;
     int sz = 0;
+#pragma unroll 8
     for (int b = 0; b < G; ++b) {
         mn = fmin(mn, psi_part[(int64_t)b * nsim + j]);
         mx = fmax(mx, phi_part[(int64_t)b * nsim + j]);
@@ -219,6 +227,13 @@ __global__ void k_scan_finish(const double* psi_part, const double* phi_part, co
     psi[j] = mn;
     phi[j] = mx;
     sizes[j] = sz;
+}
+
+// Zero the per-row counts and the MSPE flag.
+__global__ void k_scan_init(int64_t* __restrict__ counts, int64_t np, long long* __restrict__ mspe_flag) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < np) counts[i] = 0;
+    if (i == 0) *mspe_flag = 0;
 }
 
 // Row groups of a scan: enough workgroups to fill the GPU (2048), at most one per row tile and
@@ -237,10 +252,6 @@ __global__ void k_add_rows(double* S, int64_t n, int64_t m, const double* g) {
     if (idx < n * m) S[idx] += g[idx % n];
 }
 
-__global__ void k_fill_i64(int64_t* a, int64_t n, int64_t v) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) a[i] = v;
-}
 
 // t = (zhat - u) / sqrt(v) (Eq. 1); a non-positive v raises the MSPE flag.
 __global__ void k_tstat(const double* zhat, const double* v, double u, int64_t np, double* t,
@@ -475,7 +486,9 @@ struct ScanMem {
     double* gvec;
 };
 
-static void scan_carve(Carve& cv, int64_t n_p, int64_t n_o, int64_t nsim, bool need_S, size_t piece[8]) {
+constexpr int SCAN_PIECES = 8;
+
+static void scan_carve(Carve& cv, int64_t n_p, int64_t n_o, int64_t nsim, bool need_S, size_t piece[SCAN_PIECES]) {
     const int G = scan_groups(n_p, nsim);
     piece[0] = cv.add(need_S ? sizeof(double) * n_p * nsim : 0);
     piece[1] = cv.add(n_o > 0 ? sizeof(double) * n_o * nsim : 0);
@@ -487,7 +500,7 @@ static void scan_carve(Carve& cv, int64_t n_p, int64_t n_o, int64_t nsim, bool n
     piece[7] = cv.add(sizeof(double) * nsim);
 }
 
-static ScanMem scan_mem(const Carve& cv, void* base, const size_t piece[8]) {
+static ScanMem scan_mem(const Carve& cv, void* base, const size_t piece[SCAN_PIECES]) {
     ScanMem m{};
     m.S = cv.get<double>(base, piece[0]);
     m.R = cv.get<double>(base, piece[1]);
@@ -552,9 +565,7 @@ static int excursion_run(gpex_ctx_t ctx, const ScanMem& m, const double* d_M, in
     }
     const int G = scan_groups(n_p, nsim);
     const int64_t ncb = (nsim + SCOLS - 1) / SCOLS;
-    hipLaunchKernelGGL(k_fill_i64, dim3(blocks(n_p)), dim3(256), 0, s, d_counts, n_p, (int64_t)0);
-    hipLaunchKernelGGL(k_fill_i64, dim3(1), dim3(1), 0, s, reinterpret_cast<int64_t*>(ctx->d_flags + FLAG_MSPE),
-                       (int64_t)1, (int64_t)0);
+    hipLaunchKernelGGL(k_scan_init, dim3(blocks(n_p)), dim3(256), 0, s, d_counts, n_p, ctx->d_flags + FLAG_MSPE);
     if (regions) hipLaunchKernelGGL(k_tstat, dim3(blocks(n_p)), dim3(256), 0, s, d_zhat, d_v, u, n_p, m.t, fl);
     hipLaunchKernelGGL(k_scan, dim3((unsigned)G, (unsigned)ncb), dim3(256), 0, s, S, lds, n_p, nsim,
                        regions ? m.t : nullptr, u, G, reinterpret_cast<unsigned long long*>(d_counts), m.pp, m.pq,
@@ -610,7 +621,7 @@ extern "C" int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t
                              h_psi, h_phi, d_cin, d_cout));
     GPEX_HIP(ctx, hipSetDevice(ctx->device));
     Carve cv;
-    size_t piece[8];
+    size_t piece[SCAN_PIECES];
     scan_carve(cv, n_p, n_o, nsim, n_o > 0 && !d_S, piece);
     void* wsb = nullptr;
     GPEX_TRY(ws_get(ctx, WS_SCAN, cv.total, &wsb, "scan workspace"));
@@ -635,7 +646,7 @@ extern "C" int gpex_excursion_regions_noalloc(gpex_ctx_t ctx, const double* d_M,
     void* base = scratch_ptr(ctx->device);
     if (!base) return set_err(ctx, GPEX_ERR_STATE, "gpex_excursion_regions_noalloc: no scratch on this device");
     Carve cv;
-    size_t piece[8];
+    size_t piece[SCAN_PIECES];
     scan_carve(cv, n_p, 0, nsim, false, piece);   // t, partials, psi, phi
     const size_t p_g = cv.add(n_o > 0 ? sizeof(double) * n_p : 0);
     if (cv.total > SCRATCH_BYTES)
