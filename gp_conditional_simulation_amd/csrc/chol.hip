@@ -356,6 +356,10 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     // updates read the copy (the same values the kernels would convert on every load, at half or a
     // quarter of the bytes).  Two buffers, by step parity: step k's updates (look-ahead stream) still
     // read step k's copies while step k + 1's panel solves write theirs.
+    // FP16 updates read their operands from the row-major FP16 factor panels instead (the same
+    // values, with k contiguous: both operands then move in 16-byte vectors with no transposition);
+    // those panels are written by the same panel solves and never reused, so they need no copy.
+    const bool l16_ops = a->l16 != nullptr;
     auto feeds = [&](int64_t i, int64_t k, int want) {   // does tile (i, k) feed an update computing in `want`?
         for (int64_t j = k + 1; j < i; ++j)
             if (a->prec(i, j) == want) return true;
@@ -369,7 +373,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         for (int64_t i = k + 1; i < nt; ++i) {
             const int p = a->prec(i, k);
             if (p == DT_F64 && feeds(i, k, DT_F32)) any32 = need32[(size_t)(i * nt + k)] = 1;
-            if (p != DT_F16 && feeds(i, k, DT_F16)) any16 = need16[(size_t)(i * nt + k)] = 1;
+            if (p != DT_F16 && !l16_ops && feeds(i, k, DT_F16)) any16 = need16[(size_t)(i * nt + k)] = 1;
         }
     // workspace: panel copies (FP64-sized slots), diagonal scratch, operand copies, task and copy lists
     Carve cv;
@@ -430,13 +434,20 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             for (int64_t i = j; i < nt; ++i) {
                 int p = (i == j) ? DT_F64 : a->prec(i, j);
                 GemmTask g{};
-                operand(i, k, p, g.A, g.ta);
-                operand(j, k, p, g.B, g.tb);
+                if (p == DT_F16 && l16_ops) {
+                    // op(A)[r, c] = L_ik[r, c] and op(B)[c, r'] = L_jk[r', c], both k-contiguous
+                    g.A = a->l16_panel(i) + (size_t)k * nb; g.lda = i * nb; g.ta = DT_F16; g.transA = 1;
+                    g.B = a->l16_panel(j) + (size_t)k * nb; g.ldb = j * nb; g.tb = DT_F16; g.transB = 0;
+                } else {
+                    operand(i, k, p, g.A, g.ta);
+                    operand(j, k, p, g.B, g.tb);
+                    g.lda = g.ldb = nb;
+                    g.transA = 0; g.transB = 1;
+                }
                 g.C = a->tile(i, j);
-                g.lda = g.ldb = g.ldc = nb;
+                g.ldc = nb;
                 g.M = g.N = g.K = nb;
                 g.tc = (int8_t)p;
-                g.transA = 0; g.transB = 1;
                 g.alpha = -1.0;
                 g.beta = (k == 0 && p == DT_F64) ? s2_first : 1.0;   // s^2 V - L_i0 L_j0^T for FP64 tiles
                 g.tri = (i == j) ? TRI_C_LOWER : 0;   // diagonal tiles: only the lower triangle is used
