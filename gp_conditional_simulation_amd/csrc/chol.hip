@@ -351,11 +351,12 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         return compute * 1000 + g.ta * 100 + g.tb * 10 + g.tc;
     };
     // Operand copies of the panel tiles for reduced-precision updates.  A trailing update computes in
-    // its output tile's precision with the operands converted to it; a panel tile that is wider than
-    // some output it feeds gets its FP32 / FP16 rounding written once by the panel solve, and those
-    // updates read the copy (the same values the kernels would convert on every load, at half or a
-    // quarter of the bytes).  Two buffers, by step parity: step k's updates (look-ahead stream) still
-    // read step k's copies while step k + 1's panel solves write theirs.
+    // its output tile's precision with the operands converted to it; a panel tile of another
+    // precision that feeds such an output gets its FP32 / FP16 version written once by the panel
+    // solve, and those updates read the copy (the same values the kernels would convert on every
+    // load; every FP32 update then reads FP32 operands and runs one kernel signature).  Two buffers,
+    // by step parity: step k's updates (look-ahead stream) still read step k's copies while step
+    // k + 1's panel solves write theirs.
     // FP16 updates read their operands from the row-major FP16 factor panels instead (the same
     // values, with k contiguous: both operands then move in 16-byte vectors with no transposition);
     // those panels are written by the same panel solves and never reused, so they need no copy.
@@ -372,7 +373,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     for (int64_t k = 0; k + 1 < nt && a->opts.amp; ++k)
         for (int64_t i = k + 1; i < nt; ++i) {
             const int p = a->prec(i, k);
-            if (p == DT_F64 && feeds(i, k, DT_F32)) any32 = need32[(size_t)(i * nt + k)] = 1;
+            if (p != DT_F32 && feeds(i, k, DT_F32)) any32 = need32[(size_t)(i * nt + k)] = 1;
             if (p != DT_F16 && !l16_ops && feeds(i, k, DT_F16)) any16 = need16[(size_t)(i * nt + k)] = 1;
         }
     // workspace: panel copies (FP64-sized slots), diagonal scratch, operand copies, task and copy lists
