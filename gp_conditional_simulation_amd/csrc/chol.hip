@@ -350,13 +350,13 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     auto sig = [](int compute, const GemmTask& g) {
         return compute * 1000 + g.ta * 100 + g.tb * 10 + g.tc;
     };
-    // Operand copies of the panel tiles for reduced-precision updates.  A trailing update computes in
-    // its output tile's precision with the operands converted to it; a panel tile of another
-    // precision that feeds such an output gets its FP32 / FP16 version written once by the panel
-    // solve, and those updates read the copy (the same values the kernels would convert on every
-    // load; every FP32 update then reads FP32 operands and runs one kernel signature).  Two buffers,
-    // by step parity: step k's updates (look-ahead stream) still read step k's copies while step
-    // k + 1's panel solves write theirs.
+    // Operand copies of the panel tiles for the updates.  A trailing update computes in its output
+    // tile's precision with the operands converted to it; a panel tile of another precision that
+    // feeds FP32 or FP64 outputs gets its FP32 / FP64 version written once by the panel solve, and
+    // those updates read the copy (the same values the kernels would convert on every load; the
+    // updates of one step and precision then run one kernel signature, in one launch, instead of
+    // one launch per operand-type pair).  Two buffers, by step parity: step k's updates
+    // (look-ahead stream) still read step k's copies while step k + 1's panel solves write theirs.
     // FP16 updates read their operands from the row-major FP16 factor panels instead (the same
     // values, with k contiguous: both operands then move in 16-byte vectors with no transposition);
     // those panels are written by the same panel solves and never reused, so they need no copy.
@@ -368,19 +368,19 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             if (a->prec(j, i) == want) return true;
         return false;
     };
-    std::vector<uint8_t> need32((size_t)(nt * nt), 0), need16((size_t)(nt * nt), 0);
-    bool any32 = false, any16 = false;
+    std::vector<uint8_t> need32((size_t)(nt * nt), 0), need64((size_t)(nt * nt), 0);
+    bool any32 = false, any64 = false;
     for (int64_t k = 0; k + 1 < nt && a->opts.amp; ++k)
         for (int64_t i = k + 1; i < nt; ++i) {
             const int p = a->prec(i, k);
             if (p != DT_F32 && feeds(i, k, DT_F32)) any32 = need32[(size_t)(i * nt + k)] = 1;
-            if (p != DT_F16 && !l16_ops && feeds(i, k, DT_F16)) any16 = need16[(size_t)(i * nt + k)] = 1;
+            if (p != DT_F64 && feeds(i, k, DT_F64)) any64 = need64[(size_t)(i * nt + k)] = 1;
         }
     // workspace: panel copies (FP64-sized slots), diagonal scratch, operand copies, task and copy lists
     Carve cv;
     const size_t p_pws = cv.add(nt > 1 ? 8 * tile_el * (size_t)(nt - 1) : 0), p_ws = cv.add(sizeof(double) * tile_el);
     const size_t p_c32 = cv.add(any32 ? 2 * 4 * tile_el * (size_t)(nt - 1) : 0),
-                 p_c16 = cv.add(any16 ? 2 * 2 * tile_el * (size_t)(nt - 1) : 0);
+                 p_c64 = cv.add(any64 ? 2 * 8 * tile_el * (size_t)(nt - 1) : 0);
     size_t ntask = 0;
     for (int64_t k = 0; k < nt; ++k) ntask += (size_t)(nt - k - 1) + (size_t)(nt - k - 1) * (nt - k) / 2;
     const size_t p_tasks = cv.add(sizeof(GemmTask) * ntask), p_copies = cv.add(sizeof(CopyTask) * (size_t)(nt * (nt - 1) / 2));
@@ -389,14 +389,14 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     uint8_t* pws = cv.get<uint8_t>(wsb, p_pws);
     double* ws = cv.get<double>(wsb, p_ws);
     float* c32 = cv.get<float>(wsb, p_c32);
-    _Float16* c16 = cv.get<_Float16>(wsb, p_c16);
+    double* c64 = cv.get<double>(wsb, p_c64);
     auto copy32 = [&](int64_t i, int64_t k) { return c32 + ((size_t)(k % 2) * (nt - 1) + (size_t)(i - k - 1)) * tile_el; };
-    auto copy16 = [&](int64_t i, int64_t k) { return c16 + ((size_t)(k % 2) * (nt - 1) + (size_t)(i - k - 1)) * tile_el; };
+    auto copy64 = [&](int64_t i, int64_t k) { return c64 + ((size_t)(k % 2) * (nt - 1) + (size_t)(i - k - 1)) * tile_el; };
     // operand (i, k) of an update computing in `want`: the copy when there is one, else the tile
     auto operand = [&](int64_t i, int64_t k, int want, const void*& ptr, int8_t& type) {
         const int p = a->prec(i, k);
         if (want == DT_F32 && need32[(size_t)(i * nt + k)]) { ptr = copy32(i, k); type = DT_F32; return; }
-        if (want == DT_F16 && need16[(size_t)(i * nt + k)]) { ptr = copy16(i, k); type = DT_F16; return; }
+        if (want == DT_F64 && need64[(size_t)(i * nt + k)]) { ptr = copy64(i, k); type = DT_F64; return; }
         ptr = a->tile(i, k);
         type = (int8_t)p;
     };
@@ -428,7 +428,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
                 g.ldc2 = i * nb;
             }
             if (need32[(size_t)(i * nt + k)]) g.C3 = copy32(i, k);
-            if (need16[(size_t)(i * nt + k)]) g.C4 = copy16(i, k);
+            if (need64[(size_t)(i * nt + k)]) g.C4 = copy64(i, k);
             panel[sig(DT_F64, g)].push_back(g);
         }
         for (int64_t j = k + 1; j < nt; ++j)

@@ -155,11 +155,11 @@ struct GemmTask {
     // C2[col + row * ldc2].
     _Float16* C2;
     int64_t ldc2;
-    // Optional copies of the stored result in FP32 (C3) and FP16 (C4), column-major with leading
+    // Optional copies of the stored result in FP32 (C3) and FP64 (C4), column-major with leading
     // dimension ldc (the factorization's per-step operand copies of the panel tiles; same kernels
     // as C2).
     float* C3;
-    _Float16* C4;
+    double* C4;
     // FP16 destination storage between k-tasks (simulation product only, whole blocks): the
     // accumulator starts from beta C, is rounded to FP16 after every kround values of k and at the
     // end of the K loop, and alpha times it is stored.  0: off.

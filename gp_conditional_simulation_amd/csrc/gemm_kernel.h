@@ -443,7 +443,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     bool ovf = false;
     _Float16* __restrict__ C2 = T.C2;
     float* __restrict__ C3 = T.C3;
-    _Float16* __restrict__ C4 = T.C4;
+    double* __restrict__ C4 = T.C4;
     const bool use_beta = !EMU && T.beta != 0.0;   // EMU: the destination is in the accumulator
     auto epilogue = [&](auto out_tag) {   // out_tag: a value of the output element type
         typedef decltype(out_tag) TO;
@@ -503,7 +503,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
                             if (__builtin_isinf((float)h2) && !__builtin_isinf(sv)) ovf = true;
                         }
                         if (C3) C3[ci] = (float)sv;            // the values the update kernels convert on load
-                        if (C4) C4[ci] = f64_to_f16(sv);
+                        if (C4) C4[ci] = sv;
                     }
                 }
         }
