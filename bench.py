@@ -139,6 +139,8 @@ def trmm_sweep(args):
     ctx = g.Context(0)
     nsim, nb = args.sweep_nsim, 1024
     sizes = [n for n in SWEEP_N if n <= args.sweep_max_n]
+    if args.sweep_n:
+        sizes = [int(v) for v in args.sweep_n.split(",")]
     rows = []
     for n in sizes:
         x, y = syn.uniform_locations(n, 1005)
@@ -385,6 +387,7 @@ def main():
     ap.add_argument("--study-ranges", default="weak,medium,strong")
     ap.add_argument("--sweep-nsim", type=int, default=2048)
     ap.add_argument("--sweep-max-n", type=int, default=131072)
+    ap.add_argument("--sweep-n", default="", help="comma-separated sizes instead of the sweep's list (multiples of 1024)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the library's path is single-device (use --gpus 1)",
