@@ -164,6 +164,10 @@ struct GemmTask {
     // accumulator starts from beta C, is rounded to FP16 after every kround values of k and at the
     // end of the K loop, and alpha times it is stored.  0: off.
     int32_t kround;
+    // Simulation product only: the caller's part of C, rows [0, m_store) and columns [0, n_store)
+    // of the task's C (the tile padding beyond them is computed but not stored, and C is read
+    // only inside it).  0: all of C.
+    int32_t m_store, n_store;
     int32_t pad3;
 };
 

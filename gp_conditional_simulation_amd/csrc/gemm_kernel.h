@@ -292,6 +292,9 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
 
     static_assert(!EMU || (!EDGE && sizeof(CT) <= 4 && std::is_same<TC, double>::value),
                   "FP16 destination emulation: typed whole-block kernels with FP64 output");
+    // stored part of C (simulation product: the caller's rows and columns; else all of C)
+    const int m_st = (ROLE == GEMM_TRMM && T.m_store) ? T.m_store : T.M;
+    const int n_st = (ROLE == GEMM_TRMM && T.n_store) ? T.n_store : T.N;
     if constexpr (EMU) {
         // the destination enters the accumulator (it holds FP16 values: exact in FP32)
         if (T.beta != 0.0) {
@@ -304,7 +307,8 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
                     for (int r = 0; r < 4; ++r) {
                         const int row = m0 + wm * 64 + i * 16 + l % 16;
                         const int col = n0 + wn * WTN + j * 16 + acc_row<CT>(l, r);
-                        acc[i][j][r] = (float)(T.beta * Cq[(int64_t)row + (int64_t)col * T.ldc]);
+                        if (row < m_st && col < n_st)
+                            acc[i][j][r] = (float)(T.beta * Cq[(int64_t)row + (int64_t)col * T.ldc]);
                     }
         }
     }
@@ -458,8 +462,9 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int col = n0 + wn * WTN + j * 16 + acc_row<CT>(l, r);
-                        cold[j][r] = (!EDGE || (row < T.M && col < T.N)) ? Cp[(int64_t)row + (int64_t)col * T.ldc]
-                                                                         : TO(0);
+                        bool in = !EDGE || (row < T.M && col < T.N);
+                        if constexpr (ROLE == GEMM_TRMM) in = in && row < m_st && col < n_st;
+                        cold[j][r] = in ? Cp[(int64_t)row + (int64_t)col * T.ldc] : TO(0);
                     }
             }
 #pragma unroll
@@ -468,6 +473,9 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
                 for (int r = 0; r < 4; ++r) {
                     const int col = n0 + wn * WTN + j * 16 + acc_row<CT>(l, r);
                     if (EDGE && (row >= T.M || col >= T.N)) continue;
+                    if constexpr (ROLE == GEMM_TRMM) {
+                        if (row >= m_st || col >= n_st) continue;
+                    }
                     const int64_t ci = (int64_t)row + (int64_t)col * T.ldc;
                     double sv;   // the stored value, exactly, for the optional FP16 copy
                     if constexpr (sizeof(TO) == 8) {
@@ -638,6 +646,24 @@ static void launch_part(hipStream_t s, const GemmTask* d_tasks, int ntasks, cons
     }
     // everything else: element types read from the tasks, bounds-checked element loads
     const dim3 grid((unsigned)part_grid(p, ntasks, xcd));
+    if constexpr (ROLE == GEMM_TRMM) {
+        // the simulation product stores only the caller's part of C (GemmTask::m_store / n_store),
+        // which only the kernels of its own role honour
+        switch ((one.transA ? 2 : 0) | (one.transB ? 1 : 0)) {
+            case 0:
+                hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 0, 0, true, GEMM_TRMM>), grid, dim3(NTHR), 0, s,
+                                   d_tasks, one, ntasks, p.bmc, p.bnc, p.m_off, p.n_off, xcd, fl);
+                break;
+            case 2:
+                hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 1, 0, true, GEMM_TRMM>), grid, dim3(NTHR), 0, s,
+                                   d_tasks, one, ntasks, p.bmc, p.bnc, p.m_off, p.n_off, xcd, fl);
+                break;
+            default:   // the simulation product has no transposed B
+                hipLaunchKernelGGL(k_flag_badtask, dim3(1), dim3(1), 0, s, fl);
+                break;
+        }
+        return;
+    }
     switch ((one.transA ? 2 : 0) | (one.transB ? 1 : 0)) {
         case 0:
             hipLaunchKernelGGL((k_gemm_t<CT, DynT, DynT, DynT, 0, 0, true, GEMM_GENERIC>), grid, dim3(NTHR), 0, s, d_tasks,

@@ -342,15 +342,16 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
                          (j == 0 || static_cast<uint8_t*>(L->tile(i, j)) ==
                                         static_cast<uint8_t*>(L->tile(i, j - 1)) + (size_t)nb * nb * 8);
     const bool fused = (amp && L->l16) || rowpanel64;
-    // workspace: the input B, the padded M, the norm partials and the task list
+    // workspace: the input B (padded to whole tiles and 128-column blocks), the norm partials and
+    // the task list; the products write the caller's M directly (rows and columns beyond n and nsim
+    // are computed in the padding but not stored)
     const size_t ntask = fused ? (size_t)(2 * nt) : (size_t)(nt * (nt + 1) / 2);
     Carve cv;
-    const size_t p_B = cv.add((size_t)rows * cols * (amp ? 2 : 8)), p_M = cv.add(sizeof(double) * rows * cols),
-                 p_part = cv.add(sizeof(double) * nblkB), p_tasks = cv.add(sizeof(GemmTask) * ntask);
+    const size_t p_B = cv.add((size_t)rows * cols * (amp ? 2 : 8)), p_part = cv.add(sizeof(double) * nblkB),
+                 p_tasks = cv.add(sizeof(GemmTask) * ntask);
     void* wsb = nullptr;
     GPEX_TRY(ws_get(ctx, WS_SIM, cv.total, &wsb, "simulation workspace"));
     void* B = cv.get<void>(wsb, p_B);
-    double* Mp = cv.get<double>(wsb, p_M);
     double* part = cv.get<double>(wsb, p_part);
     GemmTask* d_tasks = cv.get<GemmTask>(wsb, p_tasks);
     auto* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
@@ -363,8 +364,9 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         g.A = L->tile(k, k); g.ta = DT_F64; g.lda = nb; g.transA = 0;
         g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
         g.ldb = rows; g.transB = 0;
-        g.C = Mp + k * nb; g.tc = DT_F64; g.ldc = rows;
+        g.C = d_M + k * nb; g.tc = DT_F64; g.ldc = ldm;
         g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
+        g.m_store = (int32_t)std::min<int64_t>(nb, n - k * nb); g.n_store = (int32_t)nsim;
         g.alpha = 1.0; g.beta = beta;
         g.tri = TRI_A_LOWER;   // L_kk is lower triangular
         g.kround = kround;     // cast16 of the diagonal product (Algorithm 1)
@@ -386,8 +388,9 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
                 g.A = L->tile(i, 0); g.ta = DT_F64; g.lda = nb; g.transA = 0;
             }
             g.B = B; g.tb = amp ? DT_F16 : DT_F64; g.ldb = rows; g.transB = 0;
-            g.C = Mp + i * nb; g.tc = DT_F64; g.ldc = rows;
+            g.C = d_M + i * nb; g.tc = DT_F64; g.ldc = ldm;
             g.M = (int)nb; g.N = (int)cols; g.K = (int)(i * nb);
+            g.m_store = (int32_t)std::min<int64_t>(nb, n - i * nb); g.n_store = (int32_t)nsim;
             g.alpha = 1.0; g.beta = 1.0;
             g.kround = kround;   // GEMM16 stores its destination in FP16 after each k-task
             od.push_back(g);
@@ -415,8 +418,9 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
                     g.A = L->tile(i, k); g.ta = (int8_t)ta; g.lda = nb; g.transA = 0;
                     g.B = static_cast<uint8_t*>(B) + (size_t)k * nb * (amp ? 2 : 8); g.tb = amp ? DT_F16 : DT_F64;
                     g.ldb = rows; g.transB = 0;
-                    g.C = Mp + i * nb; g.tc = DT_F64; g.ldc = rows;
+                    g.C = d_M + i * nb; g.tc = DT_F64; g.ldc = ldm;
                     g.M = (int)nb; g.N = (int)cols; g.K = (int)nb;
+                    g.m_store = (int32_t)std::min<int64_t>(nb, n - i * nb); g.n_store = (int32_t)nsim;
                     g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
                     tasks.push_back(g);
                 }
@@ -445,9 +449,10 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         r = gemm_launch(ctx, s, Lq.compute, d_tasks + Lq.b0, (int)(Lq.b1 - Lq.b0), tasks[(size_t)Lq.b0], GEMM_TRMM);
         if (ctx->timing && fused && q == 1) (void)hipEventRecord(ev[5], s);
     }
-    if (ctx->timing) (void)hipEventRecord(ev[2], s);
-    if (r >= 0) r = copy2d(ctx, s, Mp, DT_F64, rows, d_M, DT_F64, ldm, n, nsim, 1.0);
-    if (ctx->timing) (void)hipEventRecord(ev[3], s);
+    if (ctx->timing) {
+        (void)hipEventRecord(ev[2], s);
+        (void)hipEventRecord(ev[3], s);
+    }
     std::vector<double> h((size_t)nblkB);
     long long flags[FLAG_COUNT] = {};
     hipError_t e = hipMemcpyAsync(h.data(), part, sizeof(double) * nblkB, hipMemcpyDeviceToHost, s);

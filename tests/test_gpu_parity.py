@@ -363,6 +363,34 @@ def test_small_and_ragged_fp64(ctx, n, nb, nsim):
     A.close()
 
 
+@pytest.mark.parametrize("amp,nb", [(0, 256), (1, 256), (0, 320), (1, 320)],
+                         ids=["fp64-nb256", "mixed-nb256", "fp64-nb320", "mixed-nb320"])
+def test_trmm_writes_only_the_callers_part_of_m(ctx, amp, nb):
+    """The simulation product stores rows [0, n) and columns [0, nsim) of M through the caller's
+    leading dimension and nothing else: a larger buffer keeps its sentinels outside that part,
+    and the part is bitwise the result of a call with ldm = n (ragged last tile and column block;
+    tile 320 also takes the bounds-checked kernels of ragged 128-blocks)."""
+    import ctypes
+    n, nsim, extra_rows = 1000, 300, 37
+    x, y, params = setup_case(n, nb, 1.5, 0.1, 11)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=amp, tol=1e-7)
+    assert g.potrf_mp(ctx, A) == 0
+    Z = dev_cm(syn.explicit_normals(n, nsim, 2011))
+    M_ref, _ = g.trmm_sim(ctx, A, nsim, Z=Z)
+    ldm = n + extra_rows
+    sentinel = 12345.0
+    buf = torch.full((nsim + 1, ldm), sentinel, dtype=torch.float64, device="cuda:0")   # column-major ldm x (nsim + 1)
+    rc = g.lib().gpex_trmm_sim(ctx.h, A.h, nsim, 0, ctypes.c_void_p(Z.data_ptr()), ctypes.c_void_p(buf.data_ptr()),
+                               ldm, None)
+    ctx.check(rc, allow=(g.OK,))
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[:nsim, :n], M_ref.T.cpu().numpy())
+    assert np.all(got[:nsim, n:] == sentinel)
+    assert np.all(got[nsim, :] == sentinel)
+    A.close()
+
+
 def test_single_tile_mixed_precision_simulation(ctx):
     """One tile (no off-diagonal work): the mixed-precision product is the FP32 diagonal alone,
     applied to B = Z / s rounded to FP16, with the scale s of Eq. 12 (no reduced-precision tile:
