@@ -12,7 +12,10 @@
 //     kappa(L_kk) u_32 and, on strongly correlated covariances, costs positive definiteness.
 //   * trailing tiles (i, j), k < j <= i: A_ij -= L_ik L_jk^T in the precision of A_ij with the
 //     operands converted to it (FP16 on FP16 matrix cores with FP32 accumulation), one batched
-//     launch per compute precision; diagonal tiles (the SYRK tasks) are FP64.
+//     launch per compute precision; diagonal tiles (the SYRK tasks) are FP64.  The conversions
+//     are done once: the panel solve writes an FP32 / FP64 copy of each panel tile that feeds
+//     FP32 / FP64 outputs of another precision, and FP16 outputs read the row-major FP16 copy
+//     of the factor (k contiguous), so every update reads operands of its own type.
 // The T_k are kept in the handle: kriging reuses them for its blocked triangular solves.
 #include <algorithm>
 #include <cmath>

@@ -211,7 +211,9 @@ int gpex_tiled_destroy(gpex_tiled_t t);
  * correlated covariances); every trailing tile is updated in its own precision with the operands
  * converted to it (FP16 tiles on FP16 matrix cores with FP32 accumulation and one FP16 rounding per
  * update), diagonal tiles in FP64.  With amp = 1 the panel solves also write the FP16 copy of
- * each off-diagonal factor tile that gpex_trmm_sim multiplies with (Algorithm 1, cast16).
+ * each off-diagonal factor tile that gpex_trmm_sim multiplies with (Algorithm 1, cast16; the
+ * FP16 updates read their operands from it too), and FP32 / FP64 copies of the panel tiles that
+ * feed updates of another precision (workspace: up to 24 nb^2 (NT - 1) bytes).
  * *info = 0, or the 1-based column of the first non-positive pivot: then GPEX_ERR_NOT_SPD and the
  * handle is marked failed (its tiles were overwritten in place): gpex_potrf_mp, gpex_trmm_sim,
  * gpex_tiled_block and gpex_tiled_to_dense then return GPEX_ERR_STATE.  GPEX_WARN_FP16_OVERFLOW
@@ -234,12 +236,13 @@ int gpex_normals(gpex_ctx_t ctx, uint64_t seed, uint32_t stream, int64_t n, int6
  * is converted to FP16 and multiplied on FP16 matrix cores, the diagonal tile is applied in
  * FP32, all with FP32 accumulation, and M is written in FP64 (with fp16_dest_emulation the
  * running sum is kept in FP16 between k-tasks, see gpex_prec_opts); with amp = 0 everything is
- * FP64.  d_M: n x nsim, leading dimension ldm >= n.  diag (may be NULL) receives the plan's
- * diagnostics with norm_B.  Requires a factored matrix (GPEX_ERR_STATE otherwise).  Returns
- * GPEX_WARN_FP16_OVERFLOW (M is written) when an entry of Z / s overflowed in FP16.
- * Synchronises before returning.  The context keeps the workspace of its largest call (the FP16
- * or FP64 input B and a padded copy of M: about (2 or 8) + 8 bytes per element of the padded
- * n x nsim) until it is destroyed or its workspace released. */
+ * FP64.  d_M: n x nsim, leading dimension ldm >= n; exactly rows [0, n) and columns [0, nsim)
+ * are written (the products compute the tile padding but do not store it).  diag (may be NULL)
+ * receives the plan's diagnostics with norm_B.  Requires a factored matrix (GPEX_ERR_STATE
+ * otherwise).  Returns GPEX_WARN_FP16_OVERFLOW (M is written) when an entry of Z / s overflowed
+ * in FP16.  Synchronises before returning.  The context keeps the workspace of its largest call
+ * (the FP16 or FP64 input B padded to NT nb rows and a multiple of 128 columns: 2 or 8 bytes per
+ * element) until it is destroyed or its workspace released. */
 int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t l, int64_t nsim, uint64_t seed, const double* d_Z,
                   double* d_M, int64_t ldm, gpex_diag* diag);
 
