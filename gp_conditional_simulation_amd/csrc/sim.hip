@@ -66,16 +66,18 @@ __global__ void k_normals(uint64_t seed, uint32_t stream, int64_t n, int64_t nsi
 }
 
 // B (rows_pad x cols_pad, leading dim rows_pad): B_ij = Z_ij / s for i < n, j < nsim, stored in
-// FP16 (RNE) when amp, else FP64; one thread per element pair of the n x nsim block (linear index
-// l = j n + i).  Per-block partial sums of (Z/s)^2 go to part.  The padding is k_zero_pad's.
+// FP16 (RNE) when amp, else FP64; element pairs p of the n x nsim block (linear index l = j n + i)
+// in a grid-stride loop (at most MAKEB_BLOCKS workgroups, so the per-block partial sums of (Z/s)^2
+// in part stay few and k_fold_sum adds them quickly).  The padding is k_zero_pad's.
+constexpr int MAKEB_BLOCKS = 8192;
 __global__ __launch_bounds__(256) void k_make_B(const double* Zin, int64_t n, int64_t nsim,
                                                 uint64_t seed, int64_t rows_pad, double inv_s, int amp,
                                                 void* B, double* part, unsigned long long* flags) {
-    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t total = n * nsim;
     double sq = 0.0;
     bool ovf = false;
-    if (2 * p < total) {
+    for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 2 * p < total;
+         p += (int64_t)gridDim.x * blockDim.x) {
         double z[2];
         if (Zin) {
             z[0] = Zin[2 * p];
@@ -108,6 +110,23 @@ __global__ __launch_bounds__(256) void k_make_B(const double* Zin, int64_t n, in
         __syncthreads();
     }
     if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+// Sum of the nblk block partials in a fixed order (one workgroup: thread t adds partials t,
+// t + 1024, ... in turn, then a tree), so the result is reproducible; out[0] = the sum.
+constexpr int FOLD_THR = 1024;
+__global__ __launch_bounds__(FOLD_THR) void k_fold_sum(const double* __restrict__ part, int64_t nblk,
+                                                       double* __restrict__ out) {
+    __shared__ double red[FOLD_THR];
+    double s = 0.0;
+    for (int64_t b = threadIdx.x; b < nblk; b += FOLD_THR) s += part[b];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int h = FOLD_THR / 2; h > 0; h >>= 1) {
+        if ((int)threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[0] = red[0];
 }
 
 // Zeros of B outside the n x nsim block: rows [n, rows_pad) of every column and every row of
@@ -330,7 +349,7 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     const int emu = amp && L->opts.fp16_dest_emulation ? 1 : 0;
     if (emu && nb % 128 != 0)
         return set_err(ctx, GPEX_ERR_ARG, "gpex_trmm_sim: FP16 destination emulation needs a tile size that is a multiple of 128");
-    const int64_t nblkB = (n * nsim / 2 + 1 + 255) / 256;   // k_make_B: one thread per element pair
+    const int64_t nblkB = std::min<int64_t>((n * nsim / 2 + 1 + 255) / 256, MAKEB_BLOCKS);   // k_make_B workgroups
     const int64_t npad = (rows - n) * nsim + rows * (cols - nsim);
     // An all-FP64 factor whose tiles of each row are stored back to back (column-major nb x nb
     // tiles with no alignment gap): the off-diagonal tiles of row i then form one column-major
@@ -347,7 +366,7 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     // are computed in the padding but not stored)
     const size_t ntask = fused ? (size_t)(2 * nt) : (size_t)(nt * (nt + 1) / 2);
     Carve cv;
-    const size_t p_B = cv.add((size_t)rows * cols * (amp ? 2 : 8)), p_part = cv.add(sizeof(double) * nblkB),
+    const size_t p_B = cv.add((size_t)rows * cols * (amp ? 2 : 8)), p_part = cv.add(sizeof(double) * (nblkB + 1)),
                  p_tasks = cv.add(sizeof(GemmTask) * ntask);
     void* wsb = nullptr;
     GPEX_TRY(ws_get(ctx, WS_SIM, cv.total, &wsb, "simulation workspace"));
@@ -453,9 +472,12 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         (void)hipEventRecord(ev[2], s);
         (void)hipEventRecord(ev[3], s);
     }
-    std::vector<double> h((size_t)nblkB);
+    // ||Z / s||_F^2: the block partials folded on the device in a fixed order, one value back
+    double ss = 0.0;
     long long flags[FLAG_COUNT] = {};
-    hipError_t e = hipMemcpyAsync(h.data(), part, sizeof(double) * nblkB, hipMemcpyDeviceToHost, s);
+    if (diag) hipLaunchKernelGGL(k_fold_sum, dim3(1), dim3(FOLD_THR), 0, s, part, nblkB, part + nblkB);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && diag) e = hipMemcpyAsync(&ss, part + nblkB, sizeof(double), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipMemcpyAsync(flags, ctx->d_flags, sizeof(flags), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);   // also keeps `tasks` alive for its upload
     if (r < 0) return r;
@@ -470,8 +492,6 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         ctx->timings[18] = c;
         for (auto& e2 : ev) (void)hipEventDestroy(e2);
     }
-    double ss = 0.0;
-    for (double v : h) ss += v;
     if (diag) {
         *diag = L->diag;
         diag->norm_B = std::sqrt(ss);
