@@ -68,8 +68,9 @@ struct gpex_tiled_s {
     double s = 1.0;
     std::vector<double> stats;       // 3 per lower tile: sum of squares, min, max (unscaled)
     double* tinv = nullptr;          // nt tiles nb x nb FP64: inverse of each diagonal factor tile
-    // FP16 copy of the off-diagonal factor for the simulation product (amp only): tile row i as one
-    // row-major panel of nb x (i nb) at l16 + nb*nb*i(i-1)/2 (k contiguous, leading dim i nb)
+    // FP16 copy of the off-diagonal factor for the simulation product and the factorization's FP16
+    // updates (amp only): tile row i as one row-major panel of nb x (i nb) at l16 + nb*nb*i(i-1)/2
+    // (k contiguous, leading dim i nb)
     _Float16* l16 = nullptr;
     _Float16* l16_panel(int64_t i) const { return l16 + (size_t)nb * nb * (size_t)(i * (i - 1) / 2); }
     bool factored = false;

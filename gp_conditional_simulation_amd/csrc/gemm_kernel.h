@@ -477,7 +477,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
                         if (row >= m_st || col >= n_st) continue;
                     }
                     const int64_t ci = (int64_t)row + (int64_t)col * T.ldc;
-                    double sv;   // the stored value, exactly, for the optional FP16 copy
+                    double sv;   // the stored value, exactly, for the optional copies
                     if constexpr (sizeof(TO) == 8) {
                         double v = T.alpha * (double)acc[i][j][r];
                         if (use_beta) v += T.beta * (double)cold[j][r];
