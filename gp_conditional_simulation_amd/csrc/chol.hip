@@ -405,6 +405,8 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     };
     GemmTask* d_tasks = cv.get<GemmTask>(wsb, p_tasks);
     CopyTask* d_copies = cv.get<CopyTask>(wsb, p_copies);
+    tasks.reserve(ntask);
+    copies.reserve((size_t)(nt * (nt - 1) / 2));
     for (int64_t k = 0; k < nt; ++k) {
         for (int64_t i = k + 1; i < nt; ++i) {
             CopyTask c{a->tile(i, k), pws + 8 * tile_el * (i - k - 1), (int64_t)(dt_size(a->prec(i, k)) * tile_el)};
