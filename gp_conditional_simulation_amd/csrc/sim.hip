@@ -74,6 +74,7 @@ __global__ __launch_bounds__(256) void k_make_B(const double* Zin, int64_t n, in
                                                 uint64_t seed, int64_t rows_pad, double inv_s, int amp,
                                                 void* B, double* part, unsigned long long* flags) {
     const int64_t total = n * nsim;
+    const bool small = total <= (int64_t)0xffffffff;
     double sq = 0.0;
     bool ovf = false;
     for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; 2 * p < total;
@@ -85,13 +86,27 @@ __global__ __launch_bounds__(256) void k_make_B(const double* Zin, int64_t n, in
         } else {
             normal_pair(seed, 0u, (uint64_t)p, z[0], z[1]);
         }
+        // row and column of element 2p by one division (32-bit when the block allows), then of 2p + 1
+        int64_t col, row;
+        if (small) {
+            const uint32_t u = (uint32_t)(2 * p), q = u / (uint32_t)n;
+            col = q;
+            row = (int64_t)(u - q * (uint32_t)n);
+        } else {
+            col = (2 * p) / n;
+            row = 2 * p - col * n;
+        }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int64_t l = 2 * p + e;
             if (l >= total) break;
             const double b = amp ? z[e] * inv_s : z[e];
             sq += b * b;
-            const int64_t at = l % n + (l / n) * rows_pad;
+            const int64_t at = row + col * rows_pad;
+            if (++row == n) {
+                row = 0;
+                ++col;
+            }
             if (amp) {
                 const _Float16 h = f64_to_f16(b);
                 ovf |= __builtin_isinf((float)h) && !__builtin_isinf(b);
