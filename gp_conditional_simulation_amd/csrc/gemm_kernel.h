@@ -102,12 +102,17 @@ template <typename T, int N> struct VN { typedef T __attribute__((ext_vector_typ
 // is contiguous in global memory.  LDS layout: FP64/FP32 operands with CR are kept as [k][row] (row stride LDR,
 // padded so that the four lane groups of a fragment read hit different banks; stores are plain
 // vector writes); all other operands as [row][k] (k contiguous, the FP16 fragments need 8
-// consecutive k per lane).
+// consecutive k per lane).  FP16 rows are not padded: their 16-byte chunks of 8 k are stored in
+// the order chunk ^ (row mod 8), so the 16 rows that one fragment read touches at one chunk
+// index fall on 8 different chunk positions (with a padded row stride they took 2-way bank
+// conflicts).
 template <typename CT, typename T, bool CR, bool EDGE, int ROWS = 128, int THREADS = NTHR>
 struct TSlab {
     static constexpr int BK = TCfg<CT>::BK;
     static constexpr bool KROW = CR && sizeof(CT) >= 4;        // [k][row] layout
-    static constexpr int LDK = BK + TCfg<CT>::PAD;               // [row][k] row stride
+    static constexpr bool SWZ = !KROW && sizeof(CT) == 2;       // [row][k] with XOR-swizzled 16-byte chunks
+    static_assert(!SWZ || BK == 64, "the FP16 chunk swizzle assumes 8 chunks of 8 k per row");
+    static constexpr int LDK = SWZ ? BK : BK + TCfg<CT>::PAD;    // [row][k] row stride
     static constexpr int LDR = ROWS + (sizeof(CT) == 8 ? 4 : 8); // [k][row] k stride
     static constexpr int ELEMS = KROW ? BK * LDR : ROWS * LDK;
     // Micro-block path (FP16 compute, row index contiguous): each thread loads MR consecutive rows
@@ -141,7 +146,11 @@ struct TSlab {
         }
     }
 
-    __device__ __forceinline__ static int idx(int row, int k) { return KROW ? k * LDR + row : row * LDK + k; }
+    __device__ __forceinline__ static int idx(int row, int k) {
+        if constexpr (KROW) return k * LDR + row;
+        if constexpr (SWZ) return row * LDK + ((((k >> 3) ^ (row & 7)) << 3) | (k & 7));
+        return row * LDK + k;
+    }
 
     // Vector q of this thread's share of the slab at (r0, k0), from global memory into registers.
     __device__ __forceinline__ void load_q(int q, gptr<T> base, int64_t ld, int r0, int k0, int R, int K, int t) {
@@ -218,8 +227,17 @@ struct TSlab {
         } else {
             constexpr int TPR = BK / VE;
             int r = t / TPR + (THREADS / TPR) * q, k = (t % TPR) * VE;
+            if constexpr (SWZ) {
+                // VE consecutive k (a whole or half 16-byte chunk) stay together under the swizzle
+                typedef typename VN<CT, VE>::type WT;
+                WT w;
 #pragma unroll
-            for (int e = 0; e < VE; ++e) sm[idx(r, k + e)] = v[q][e];
+                for (int e = 0; e < VE; ++e) w[e] = v[q][e];
+                *reinterpret_cast<WT*>(&sm[idx(r, k)]) = w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < VE; ++e) sm[idx(r, k + e)] = v[q][e];
+            }
         }
     }
 
