@@ -325,8 +325,8 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
                     for (int r = 0; r < 4; ++r) {
                         const int row = m0 + wm * 64 + i * 16 + l % 16;
                         const int col = n0 + wn * WTN + j * 16 + acc_row<CT>(l, r);
-                        if (row < m_st && col < n_st)
-                            acc[i][j][r] = (float)(T.beta * Cq[(int64_t)row + (int64_t)col * T.ldc]);
+                        // clamped, in-bounds reads outside the stored part (never written back)
+                        acc[i][j][r] = (float)(T.beta * Cq[(int64_t)min(row, m_st - 1) + (int64_t)min(col, n_st - 1) * T.ldc]);
                     }
         }
     }
@@ -480,9 +480,15 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int col = n0 + wn * WTN + j * 16 + acc_row<CT>(l, r);
-                        bool in = !EDGE || (row < T.M && col < T.N);
-                        if constexpr (ROLE == GEMM_TRMM) in = in && row < m_st && col < n_st;
-                        cold[j][r] = in ? Cp[(int64_t)row + (int64_t)col * T.ldc] : TO(0);
+                        if constexpr (ROLE == GEMM_TRMM && !EDGE) {
+                            // outside the stored part (never written back) read a clamped, in-bounds
+                            // element: the loads stay unconditional and issue together
+                            cold[j][r] = Cp[(int64_t)min(row, m_st - 1) + (int64_t)min(col, n_st - 1) * T.ldc];
+                        } else {
+                            bool in = !EDGE || (row < T.M && col < T.N);
+                            if constexpr (ROLE == GEMM_TRMM) in = in && row < m_st && col < n_st;
+                            cold[j][r] = in ? Cp[(int64_t)row + (int64_t)col * T.ldc] : TO(0);
+                        }
                     }
             }
 #pragma unroll
