@@ -286,7 +286,18 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
         task = (int)(b / bpt);
         blk = (int)(b % bpt);
     }
-    const GemmTask T = tasks ? tasks[task] : one;
+    // The task through the scalar data cache in one go (the index is the same for the whole
+    // workgroup): field-by-field loads through the vector path waited for each other in turn.
+    GemmTask T = one;
+    if (tasks) {
+        static_assert(sizeof(GemmTask) % 8 == 0, "task read as 8-byte words");
+        const __attribute__((address_space(4))) uint64_t* src =
+            (const __attribute__((address_space(4))) uint64_t*)(tasks + task);
+        uint64_t w[sizeof(GemmTask) / 8];
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(GemmTask) / 8); ++i) w[i] = src[i];
+        __builtin_memcpy(&T, w, sizeof(GemmTask));
+    }
     if (!type_ok<TA>(T.ta) || !type_ok<TB>(T.tb) || !type_ok<TC>(T.tc) || T.transA != TRA ||
         (T.transB != 0) != (TRB != 0)) {
         if (threadIdx.x == 0 && flags) atomicOr(&flags[FLAG_BADTASK], 1ull);
