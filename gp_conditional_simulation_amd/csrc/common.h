@@ -187,6 +187,7 @@ enum : int { TRI_C_LOWER = 1, TRI_A_LOWER = 2, TRI_B_UPPER = 4 };
 enum : int { GEMM_GENERIC = 0, GEMM_UPDATE = 1, GEMM_TRMM = 2 };
 // role only names the kernel symbols (trailing updates, simulation product, the rest) so that
 // kernel traces attribute their time; the launch choices follow the task types.
+extern int g_panel16;    // FP16 simulation-product row panels on 256 x 256 blocks when they fit (0: never)
 extern int g_f16_grid;   // wave grid of FP16 TRMM launches (-1 auto, 0: 2 x 2, otherwise 2 x 4)
 int gemm_launch(gpex_ctx_t ctx, hipStream_t s, int compute, const GemmTask* d_tasks, int ntasks,
                 const GemmTask& one, int role = GEMM_GENERIC);

@@ -9,6 +9,9 @@ namespace gpex {
 // still gives at least 2048 workgroups, else 2 x 2), 0 = 2 x 2 waves (128 x 128), otherwise 2 x 4
 // (128 x 256).
 int g_f16_grid = -1;
+// Row panels of the FP16 simulation product on the 256 x 256 kernel (panel16.h) when their shape
+// allows; 0 keeps them on the general kernel.
+int g_panel16 = 1;
 
 int gemm_launch(gpex_ctx_t ctx, hipStream_t s, int compute, const GemmTask* d_tasks, int ntasks,
                 const GemmTask& one, int role) {

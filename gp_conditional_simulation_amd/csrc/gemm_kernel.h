@@ -561,6 +561,12 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     if (ovf && flags) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
 }
 
+}  // namespace gpex
+
+#include "panel16.h"
+
+namespace gpex {
+
 static __global__ void k_flag_badtask(unsigned long long* flags) {
     if (flags) atomicOr(&flags[FLAG_BADTASK], 1ull);
 }
@@ -585,6 +591,19 @@ static int try_typed(hipStream_t s, const GemmTask* d_tasks, int ntasks, const G
     if (one.ta != DtOf<TA>::v || one.tb != DtOf<TB>::v || one.tc != DtOf<TC>::v) return 0;
     if (one.transA != TRA || (one.transB != 0) != (TRB != 0)) return 0;
     const unsigned grid = (unsigned)part_grid(p, ntasks, xcd);
+    if constexpr (sizeof(CT) == 2 && ROLE == GEMM_TRMM && TRA == 1 && TRB == 0 && std::is_same<TA, _Float16>::value &&
+                  std::is_same<TB, _Float16>::value && std::is_same<TC, double>::value) {
+        // row panels of the simulation product: 256 x 256 blocks (panel16.h) when the part is all
+        // of C and that still leaves at least 1024 workgroups
+        const bool whole = p.fast && p.m_off == 0 && p.n_off == 0 && p.bmc * BM == one.M && p.bnc * BN == one.N;
+        if (g_panel16 && whole && panel16_fits(one) &&
+            (int64_t)ntasks * (one.M / P16_BM) * (one.N / P16_BN) >= 1024) {
+            const Part w{0, 0, one.M / P16_BM, one.N / P16_BN, true};
+            hipLaunchKernelGGL(k_panel16<0>, dim3((unsigned)part_grid(w, ntasks, xcd)), dim3(P16_THR), 0, s, d_tasks,
+                               ntasks, w.bmc, w.bnc, xcd, fl);
+            return 1;
+        }
+    }
     if constexpr (ROLE == GEMM_TRMM && sizeof(CT) <= 4 && std::is_same<TC, double>::value) {
         if (one.kround) {   // FP16 destination emulation: 128 x 128 blocks, whole blocks only
             if (!p.fast) return 0;

@@ -391,6 +391,41 @@ def test_trmm_writes_only_the_callers_part_of_m(ctx, amp, nb):
     A.close()
 
 
+def test_trmm_256_blocks_rows_and_store_guard(ctx):
+    """Row panels large enough for the 256 x 256 FP16 kernel (65 panels x 2 x 8 blocks): sampled
+    rows of M, including rows of every 64-row wave group and of the ragged last tile row, equal
+    the factor's row times the oracle's seeded normals (to FP16 accuracy), and a call through a
+    larger leading dimension stores exactly rows [0, n) and columns [0, nsim), bitwise as with
+    ldm = n."""
+    import ctypes
+    n, nb, nsim, seed, extra_rows = 33500, 512, 2000, 2013, 37
+    x, y, params = setup_case(n, nb, 1.5, 0.1, 13)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=1e-8)
+    assert g.potrf_mp(ctx, A) == 0
+    M_ref, _ = g.trmm_sim(ctx, A, nsim, seed=seed)
+    # tile row 1 (rows 512-1023): every 64-row wave group of both 256-row blocks; tile row 0 has
+    # only its diagonal product; rows 33280-33499 are the ragged last tile row
+    rows = [0, 512, 600, 700, 800, 900, 1023, 20000, 33279, 33280, 33499]
+    Z = oracle.normals(seed, 0, n, nsim, rows=(0, max(rows) + 1))
+    Mr = M_ref[rows].cpu().numpy()
+    for k, r in enumerate(rows):
+        lr = A.block(r, 0, 1, r + 1).cpu().numpy()[0]
+        ref = lr @ Z[:r + 1]
+        er = np.linalg.norm(Mr[k] - ref) / np.linalg.norm(ref)
+        assert er <= 1e-2, (r, er)
+    ldm = n + extra_rows
+    sentinel = 12345.0
+    buf = torch.full((nsim + 1, ldm), sentinel, dtype=torch.float64, device="cuda:0")   # column-major ldm x (nsim + 1)
+    rc = g.lib().gpex_trmm_sim(ctx.h, A.h, nsim, seed, None, ctypes.c_void_p(buf.data_ptr()), ldm, None)
+    ctx.check(rc, allow=(g.OK,))
+    torch.cuda.synchronize()
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[:nsim, :n], M_ref.T.cpu().numpy())
+    assert np.all(got[:nsim, n:] == sentinel)
+    assert np.all(got[nsim, :] == sentinel)
+    A.close()
+
+
 def test_single_tile_mixed_precision_simulation(ctx):
     """One tile (no off-diagonal work): the mixed-precision product is the FP32 diagonal alone,
     applied to B = Z / s rounded to FP16, with the scale s of Eq. 12 (no reduced-precision tile:
