@@ -10,8 +10,9 @@
 //
 // Design (gfx950, wave64):
 //   * A workgroup computes one block of C: 2 x 2 waves of 64 x 64 (128 x 128, 256 threads), or
-//     2 x 4 waves (128 x 256) for large FP16 simulation products.  Each wave's 64 x 64 sub-block
-//     is 4 x 4 matrix-core tiles of 16 x 16, accumulated in vector registers.
+//     2 x 4 waves (128 x 256) for large simulation products.  Each wave's 64 x 64 sub-block is
+//     4 x 4 matrix-core tiles of 16 x 16, accumulated in vector registers.  Large FP16 row panels
+//     of the simulation product go to a dedicated 256 x 256 kernel instead (panel16.h).
 //   * FP64: v_mfma_f64_16x16x4 (lane l, acc r -> row l/16 + 4r, col l%16).
 //     FP32: v_mfma_f32_16x16x4 (row 4(l/16) + r, col l%16).
 //     FP16: v_mfma_f32_16x16x32_f16 with FP32 accumulation (row 4(l/16) + r, col l%16).
