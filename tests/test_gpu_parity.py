@@ -394,9 +394,9 @@ def test_trmm_writes_only_the_callers_part_of_m(ctx, amp, nb):
 def test_trmm_256_blocks_rows_and_store_guard(ctx):
     """Row panels large enough for the 256 x 256 FP16 kernel (65 panels x 2 x 8 blocks): sampled
     rows of M, including rows of every 64-row wave group and of the ragged last tile row, equal
-    the factor's row times the oracle's seeded normals (to FP16 accuracy), and a call through a
+    the factor's row times the oracle's seeded normals (to FP16 accuracy), a call through a
     larger leading dimension stores exactly rows [0, n) and columns [0, nsim), bitwise as with
-    ldm = n."""
+    ldm = n, and the general kernel gives the same columns bitwise."""
     import ctypes
     n, nb, nsim, seed, extra_rows = 33500, 512, 2000, 2013, 37
     x, y, params = setup_case(n, nb, 1.5, 0.1, 13)
@@ -423,6 +423,11 @@ def test_trmm_256_blocks_rows_and_store_guard(ctx):
     assert np.array_equal(got[:nsim, :n], M_ref.T.cpu().numpy())
     assert np.all(got[:nsim, n:] == sentinel)
     assert np.all(got[nsim, :] == sentinel)
+    # 1,920 columns (not a multiple of 256) take the general 128 x 256 kernel; column j of the
+    # seeded normals does not depend on nsim and both kernels sum each output's k in the same
+    # order, so the shared columns agree bitwise
+    M_gen, _ = g.trmm_sim(ctx, A, 1920, seed=seed)
+    assert np.array_equal(M_gen.cpu().numpy(), M_ref[:, :1920].cpu().numpy())
     A.close()
 
 
