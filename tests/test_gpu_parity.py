@@ -76,6 +76,36 @@ def test_cov_gen_stats_and_values(ctx, case):
     A.close()
 
 
+@pytest.mark.parametrize("kind,nu", [(0, 0.5), (0, 1.5), (0, 2.5), (1, 0.5)], ids=["m12", "m32", "m52", "gauss"])
+@pytest.mark.parametrize("beta", [1e-7, 1.6e-3, 40.0])
+def test_cov_gen_extreme_ranges(ctx, kind, nu, beta):
+    """Ranges at the ends of the exponent: 1e-7 (Matern: every off-diagonal entry is an exact zero;
+    most exponents are clamped before their integer part is taken), 1.6e-3 (entries from sigma^2
+    down through the subnormal range to zero) and 40 (every entry near sigma^2).  The exponent's argument x (r for
+    the Matern models, d^2 / range for the Gaussian) carries a few ulps of rounding on either side,
+    so an entry may differ by about x ulps relative; subnormal entries by their spacing."""
+    n, nb, sigma2 = 700, 128, 2.5
+    x, y = syn.uniform_locations(n, 21)
+    x, y, _ = syn.ordered_locations(x, y)
+    params = {"kind": kind, "sigma2": sigma2, "range": beta, "nu": nu, "nugget": 1e-4}
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=0)
+    V = oracle.cov_matrix(x, y, kind, sigma2, beta, nu, nugget=1e-4)
+    Vg = A.to_dense().cpu().numpy()
+    A.close()
+    low = np.tril_indices(n)
+    d2 = (x[:, None] - x[None, :]) ** 2 + (y[:, None] - y[None, :]) ** 2
+    arg = d2 / beta if kind == 1 else np.sqrt(d2) / beta
+    err = np.abs(Vg[low] - V[low])
+    bound = 1e-300 + (1e-14 + 8 * np.finfo(float).eps * arg[low]) * np.abs(V[low])
+    assert np.all(err <= bound), float(np.max(err / bound))
+    if beta == 1e-7 and kind == 0:
+        off = np.tril_indices(n, -1)
+        assert np.all(Vg[off] == 0.0) and np.all(np.diag(Vg) == sigma2 + 1e-4)
+    if beta == 1.6e-3:
+        tiny = V[low][(V[low] > 0) & (V[low] < np.finfo(float).tiny)]
+        assert tiny.size > 0   # the case reaches subnormal entries
+
+
 @pytest.mark.parametrize("tol", [1e-9, 1e-6, 1e-3])
 def test_plan_from_device_stats_matches_oracle_plan(ctx, tol):
     n, nb = 3000, 160
