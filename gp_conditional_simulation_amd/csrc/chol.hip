@@ -482,7 +482,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     if (!copies.empty()) GPEX_HIP(ctx, hipMemcpyAsync(d_copies, copies.data(), sizeof(CopyTask) * copies.size(), hipMemcpyHostToDevice, s));
     GPEX_HIP(ctx, hipMemsetAsync(ctx->d_flags + FLAG_INFO, 0, sizeof(long long) * (FLAG_BADTASK + 1), s));
 
-    Timer tm{ctx};
+    Timer tm{ctx, {}, 0};
     struct Rec { hipEvent_t b, e; int prec; };
     std::vector<Rec> recs;
     hipEvent_t e_all0 = nullptr, e_all1 = nullptr;

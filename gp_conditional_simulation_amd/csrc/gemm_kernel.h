@@ -568,7 +568,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
 
 namespace gpex {
 
-static __global__ void k_flag_badtask(unsigned long long* flags) {
+__attribute__((unused)) static __global__ void k_flag_badtask(unsigned long long* flags) {
     if (flags) atomicOr(&flags[FLAG_BADTASK], 1ull);
 }
 
@@ -578,7 +578,7 @@ struct Part {
     bool fast;   // whole blocks and slabs with aligned operands: vector loads, no bounds checks
 };
 
-static int64_t part_grid(const Part& p, int ntasks, int xcd) {
+static inline int64_t part_grid(const Part& p, int ntasks, int xcd) {
     const int64_t bpt = (int64_t)p.bmc * p.bnc;
     return xcd ? (int64_t)8 * ((ntasks + 7) / 8) * bpt : (int64_t)ntasks * bpt;
 }

@@ -70,6 +70,7 @@ __global__ __launch_bounds__(256) void k_mspe(const double* W, const double* Vop
                                               int64_t ldx, const double* H, int ktr, int64_t no,
                                               int64_t np, double sigma2, double* v) {
     int64_t j = blockIdx.x;
+    if (j >= np) return;
     double h0 = 0, h1 = 0, h2 = 0;
     if (ktr) { h0 = H[3 * j]; h1 = H[3 * j + 1]; h2 = H[3 * j + 2]; }
     double acc = 0.0;
@@ -179,7 +180,7 @@ extern "C" int gpex_krige(gpex_ctx_t ctx, const double* d_loc_o, int64_t n_o, co
     *info = 0;
     gpex_cov_params cp = *params;
     cp.nugget = tau2;
-    gpex_prec_opts po{0, 0.0, 0, 0, 0};
+    gpex_prec_opts po{0, 0.0, 0, 0, 0, 0};
     gpex_tiled_t Sy = nullptr;
     int r = gpex_cov_gen(ctx, d_loc_o, n_o, nullptr, &cp, nb, &po, &Sy, nullptr);
     if (r < 0) return r;
