@@ -31,7 +31,7 @@ EXPORTS = ["gpex_version", "gpex_ctx_create", "gpex_ctx_destroy", "gpex_ctx_rele
            "gpex_tiled_info", "gpex_tiled_stats", "gpex_tiled_to_dense", "gpex_tiled_block", "gpex_tiled_block_raw",
            "gpex_tiled_destroy",
            "gpex_potrf_mp", "gpex_normals", "gpex_trmm_sim", "gpex_krige", "gpex_excursion_regions",
-           "gpex_excursion_regions_noalloc",
+           "gpex_excursion_regions_below", "gpex_excursion_regions_noalloc",
            "gpex_plan", "gpex_ctx_set_timing", "gpex_ctx_timings"]
 
 
@@ -107,6 +107,7 @@ def lib():
         L.gpex_excursion_regions.argtypes = [P, P, I64, I64, I64, I64, P, P, P, P, D, D, P, P, P, P, P, P, P,
                                              C.POINTER(RegionStats)]
         L.gpex_excursion_regions_noalloc.argtypes = L.gpex_excursion_regions.argtypes
+        L.gpex_excursion_regions_below.argtypes = L.gpex_excursion_regions.argtypes
         L.gpex_plan.argtypes = [P, I64, C.POINTER(PrecOpts), P, C.POINTER(Diag)]
         L.gpex_ctx_set_timing.argtypes = [P, I]
         L.gpex_ctx_timings.argtypes = [P, P]
@@ -368,9 +369,10 @@ def krige(ctx: Context, loc_o, n_o: int, loc_p, n_p: int, y_o, k_trend: int, par
 
 
 def excursion_regions(ctx: Context, M, n_p: int, n_o: int, nsim: int, u: float, level: float = 0.9, W=None,
-                      y_o=None, zhat=None, v=None, want_S=False, noalloc=False, counts=None, sizes=None):
+                      y_o=None, zhat=None, v=None, want_S=False, noalloc=False, counts=None, sizes=None,
+                      below=False):
     """gpex_excursion_regions (gpex_excursion_regions_noalloc with noalloc=True, which needs
-    want_S when n_o > 0).  M: column-major (n_p + n_o) x nsim view; W: column-major n_o x n_p view.
+    want_S when n_o > 0; gpex_excursion_regions_below, the negative excursion set, with below=True).  M: column-major (n_p + n_o) x nsim view; W: column-major n_o x n_p view.
     counts / sizes: optional int64 (n_p) / int32 (nsim) device outputs to reuse (the call writes
     every entry).  Returns dict with counts, sizes, and (with zhat) psi, phi, cin, cout, q_in,
     q_out, n_psi, n_phi, status."""
@@ -394,7 +396,10 @@ def excursion_regions(ctx: Context, M, n_p: int, n_o: int, nsim: int, u: float, 
         cout = torch.zeros(n_p, dtype=torch.uint8, device=dev)
     if M.shape[0] != ldm or M.shape[1] != nsim:
         raise ValueError("M must be (n_p + n_o) x nsim")
-    fn = lib().gpex_excursion_regions_noalloc if noalloc else lib().gpex_excursion_regions
+    if noalloc and below:
+        raise ValueError("the allocation-free entry point computes the positive excursion set only")
+    fn = (lib().gpex_excursion_regions_noalloc if noalloc else
+          lib().gpex_excursion_regions_below if below else lib().gpex_excursion_regions)
     rc = fn(
         ctx.h, _cm(M), ldm, n_p, n_o, nsim, _cm(W), _ptr(y_o), _ptr(zhat), _ptr(v), u, level,
         _ptr(counts), _ptr(sizes), psi.ctypes.data if psi is not None else None,

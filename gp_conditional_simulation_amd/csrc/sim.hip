@@ -170,9 +170,10 @@ constexpr int SBATCH = 16;               // loads in flight per thread
 // (column, quarter of the rows): min of t over the >= rows, max over the <= rows, size of the >=
 // set, kept in registers across the group's tiles.  The quarters are folded in order at the end
 // and written as the group's partials of each column; k_scan_finish folds the groups.  Rows beyond
-// np and columns beyond nsim carry no flags.
+// np and columns beyond nsim carry no flags.  sgn = -1 scans -S against -u (the lower excursion
+// set by sign reversal; sgn = 1 leaves every value as it is).
 __global__ __launch_bounds__(256) void k_scan(const double* __restrict__ S, int64_t lds, int64_t np,
-                                              int64_t nsim, const double* __restrict__ t, double u, int G,
+                                              int64_t nsim, const double* __restrict__ t, double sgn, double u, int G,
                                               unsigned long long* __restrict__ counts,
                                               double* __restrict__ psi_part, double* __restrict__ phi_part,
                                               int* __restrict__ size_part) {
@@ -200,10 +201,12 @@ __global__ __launch_bounds__(256) void k_scan(const double* __restrict__ S, int6
                 double v[SBATCH];
 #pragma unroll
                 for (int k = 0; k < SBATCH; ++k) v[k] = col[(int64_t)min(cb + k, ncol - 1) * lds];
+                const double su = sgn * u;
 #pragma unroll
                 for (int k = 0; k < SBATCH; ++k) {
                     const bool ok = cb + k < ncol;
-                    const bool a = ok && v[k] >= u, b = ok && v[k] <= u;
+                    const double w = sgn * v[k];
+                    const bool a = ok && w >= su, b = ok && w <= su;
                     fg |= (uint64_t)a << (cb + k);
                     fe |= (uint64_t)b << (cb + k);
                     cnt += a;
@@ -287,8 +290,9 @@ __global__ void k_add_rows(double* S, int64_t n, int64_t m, const double* g) {
 }
 
 
-// t = (zhat - u) / sqrt(v) (Eq. 1); a non-positive v raises the MSPE flag.
-__global__ void k_tstat(const double* zhat, const double* v, double u, int64_t np, double* t,
+// t = (zhat - u) / sqrt(v) (Eq. 1) of the field times sgn (sgn = -1: -zhat against -u); a
+// non-positive v raises the MSPE flag.
+__global__ void k_tstat(const double* zhat, const double* v, double sgn, double u, int64_t np, double* t,
                         unsigned long long* flags) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= np) return;
@@ -298,7 +302,7 @@ __global__ void k_tstat(const double* zhat, const double* v, double u, int64_t n
         t[i] = NAN;
         return;
     }
-    t[i] = (zhat[i] - u) / sqrt(vi);
+    t[i] = (sgn * zhat[i] - sgn * u) / sqrt(vi);
 }
 
 // R = y_o 1^T - M_o (n_o x nsim, leading dim n_o).
@@ -574,7 +578,7 @@ static int excursion_run(gpex_ctx_t ctx, const ScanMem& m, const double* d_M, in
                          int64_t nsim, const double* d_W, const double* d_y_o, const double* d_zhat,
                          const double* d_v, double u, double level_c, int64_t* d_counts, int32_t* d_sizes,
                          double* h_psi, double* h_phi, uint8_t* d_cin, uint8_t* d_cout, double* d_S,
-                         gpex_region_stats* st) {
+                         gpex_region_stats* st, double sgn) {
     hipStream_t s = ctx->stream;
     auto* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
     const bool regions = d_zhat != nullptr;
@@ -606,9 +610,9 @@ static int excursion_run(gpex_ctx_t ctx, const ScanMem& m, const double* d_M, in
     const int G = scan_groups(n_p, nsim);
     const int64_t ncb = (nsim + SCOLS - 1) / SCOLS;
     hipLaunchKernelGGL(k_scan_init, dim3(blocks(n_p)), dim3(256), 0, s, d_counts, n_p, ctx->d_flags + FLAG_MSPE);
-    if (regions) hipLaunchKernelGGL(k_tstat, dim3(blocks(n_p)), dim3(256), 0, s, d_zhat, d_v, u, n_p, m.t, fl);
+    if (regions) hipLaunchKernelGGL(k_tstat, dim3(blocks(n_p)), dim3(256), 0, s, d_zhat, d_v, sgn, u, n_p, m.t, fl);
     hipLaunchKernelGGL(k_scan, dim3((unsigned)G, (unsigned)ncb), dim3(256), 0, s, S, lds, n_p, nsim,
-                       regions ? m.t : nullptr, u, G, reinterpret_cast<unsigned long long*>(d_counts), m.pp, m.pq,
+                       regions ? m.t : nullptr, sgn, u, G, reinterpret_cast<unsigned long long*>(d_counts), m.pp, m.pq,
                        m.sp);
     hipLaunchKernelGGL(k_scan_finish, dim3(blocks(nsim)), dim3(256), 0, s, m.pp, m.pq, m.sp, G, nsim, m.psi, m.phi,
                        d_sizes);
@@ -651,11 +655,11 @@ static int excursion_run(gpex_ctx_t ctx, const ScanMem& m, const double* d_M, in
     return GPEX_OK;
 }
 
-extern "C" int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p,
-                                      int64_t n_o, int64_t nsim, const double* d_W, const double* d_y_o,
-                                      const double* d_zhat, const double* d_v, double u, double level_c,
-                                      int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
-                                      uint8_t* d_cin, uint8_t* d_cout, double* d_S, gpex_region_stats* st) {
+static int excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p, int64_t n_o,
+                             int64_t nsim, const double* d_W, const double* d_y_o, const double* d_zhat,
+                             const double* d_v, double u, double level_c, int64_t* d_counts, int32_t* d_sizes,
+                             double* h_psi, double* h_phi, uint8_t* d_cin, uint8_t* d_cout, double* d_S,
+                             gpex_region_stats* st, double sgn) {
     if (!ctx) return GPEX_ERR_ARG;
     GPEX_TRY(excursion_check(ctx, d_M, ldm, n_p, n_o, nsim, d_W, d_y_o, d_zhat, d_v, level_c, d_counts, d_sizes,
                              h_psi, h_phi, d_cin, d_cout));
@@ -666,7 +670,26 @@ extern "C" int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t
     void* wsb = nullptr;
     GPEX_TRY(ws_get(ctx, WS_SCAN, cv.total, &wsb, "scan workspace"));
     return excursion_run(ctx, scan_mem(cv, wsb, piece), d_M, ldm, n_p, n_o, nsim, d_W, d_y_o, d_zhat, d_v, u, level_c,
-                         d_counts, d_sizes, h_psi, h_phi, d_cin, d_cout, d_S, st);
+                         d_counts, d_sizes, h_psi, h_phi, d_cin, d_cout, d_S, st, sgn);
+}
+
+extern "C" int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p,
+                                      int64_t n_o, int64_t nsim, const double* d_W, const double* d_y_o,
+                                      const double* d_zhat, const double* d_v, double u, double level_c,
+                                      int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
+                                      uint8_t* d_cin, uint8_t* d_cout, double* d_S, gpex_region_stats* st) {
+    return excursion_regions(ctx, d_M, ldm, n_p, n_o, nsim, d_W, d_y_o, d_zhat, d_v, u, level_c, d_counts, d_sizes,
+                             h_psi, h_phi, d_cin, d_cout, d_S, st, 1.0);
+}
+
+// The lower excursion set {y <= u} by sign reversal: the same computation on -S, -u and -zhat.
+extern "C" int gpex_excursion_regions_below(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p,
+                                            int64_t n_o, int64_t nsim, const double* d_W, const double* d_y_o,
+                                            const double* d_zhat, const double* d_v, double u, double level_c,
+                                            int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
+                                            uint8_t* d_cin, uint8_t* d_cout, double* d_S, gpex_region_stats* st) {
+    return excursion_regions(ctx, d_M, ldm, n_p, n_o, nsim, d_W, d_y_o, d_zhat, d_v, u, level_c, d_counts, d_sizes,
+                             h_psi, h_phi, d_cin, d_cout, d_S, st, -1.0);
 }
 
 // Allocation-free variant: the temporaries live in the library's fixed per-GPU scratch array and
@@ -700,7 +723,7 @@ extern "C" int gpex_excursion_regions_noalloc(gpex_ctx_t ctx, const double* d_M,
     const bool serial = ctx->serial;
     ctx->serial = true;
     const int r = excursion_run(ctx, m, d_M, ldm, n_p, n_o, nsim, d_W, d_y_o, d_zhat, d_v, u, level_c, d_counts,
-                                d_sizes, h_psi, h_phi, d_cin, d_cout, d_S, st);
+                                d_sizes, h_psi, h_phi, d_cin, d_cout, d_S, st, 1.0);
     ctx->serial = serial;
     return r;
 }

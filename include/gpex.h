@@ -280,6 +280,19 @@ int gpex_excursion_regions(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64
                            int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
                            uint8_t* d_cin, uint8_t* d_cout, double* d_S, gpex_region_stats* st);
 
+/* The negative excursion set A-_u(Z) = {s : Z(s) <= u} ("Mixed-Precision GPU Acceleration for
+ * Confidence Regions of Spatial Excursion Sets", Sec. III: negative excursions by reversing the
+ * sign of the process and the threshold): the same arguments, conditioning and outputs as
+ * gpex_excursion_regions, computed for -S, -u and -zhat, i.e. d_counts[i] = #{j : S_ij <= u},
+ * d_sizes[j] = #{i : S_ij <= u}, t = (u - zhat) / sqrt(v), psi_j = min of t over {S_ij <= u},
+ * phi_j = max of t over {S_ij >= u}, and q_out, q_in, d_cout, d_cin from them as above (they bound
+ * the negative excursion set).  d_S (when given) receives S itself, not -S.  Same return codes. */
+int gpex_excursion_regions_below(gpex_ctx_t ctx, const double* d_M, int64_t ldm, int64_t n_p,
+                                 int64_t n_o, int64_t nsim, const double* d_W, const double* d_y_o,
+                                 const double* d_zhat, const double* d_v, double u, double level_c,
+                                 int64_t* d_counts, int32_t* d_sizes, double* h_psi, double* h_phi,
+                                 uint8_t* d_cin, uint8_t* d_cout, double* d_S, gpex_region_stats* st);
+
 /* Allocation-free variant of gpex_excursion_regions, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * Same arguments, results and return codes, with these differences:

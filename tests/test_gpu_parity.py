@@ -354,6 +354,59 @@ def test_conditioning_scan_and_regions(ctx):
     A.close()
 
 
+def test_negative_excursion_set_by_sign_reversal(ctx):
+    """The negative excursion set {Z <= u} ("Mixed-Precision GPU Acceleration for Confidence Regions
+    of Spatial Excursion Sets", Sec. III: reverse the sign of the process and the threshold):
+    counts and sizes are #{S <= u} counted directly; psi, phi, the quantiles and both regions are
+    the oracle's scan and calibration of -S against -u with t = (u - zhat) / sqrt(v); and the call
+    agrees bitwise with the positive-set call on -M, -y_o, -u and -zhat (negation is exact in every
+    rounding of the conditioning)."""
+    n_o, n_p, nb, nsim, u, c = 1200, 800, 256, 300, 0.5, 0.9
+    xo, yo, xp, yp, y_obs = _krige_case(n_o, n_p, 21)
+    params = {"kind": 0, "sigma2": 1.0, "range": 0.1, "nu": 1.5}
+    W, zhat, v, info = g.krige(ctx, dev(np.r_[xo, yo]), n_o, dev(np.r_[xp, yp]), n_p, dev(y_obs), 3, params, 0.01, nb)
+    assert info == 0
+    x = np.r_[xp, xo]; y = np.r_[yp, yo]
+    diag_add = np.r_[np.zeros(n_p), np.full(n_o, 0.01)]
+    n = n_p + n_o
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, dict(params, nugget=0.0), nb, amp=0, diag_add=dev(diag_add))
+    assert g.potrf_mp(ctx, A) == 0
+    Z = syn.explicit_normals(n, nsim, 2006)
+    M, _ = g.trmm_sim(ctx, A, nsim, Z=dev_cm(Z))
+    out = g.excursion_regions(ctx, M, n_p, n_o, nsim, u, c, W=W, y_o=dev(y_obs), zhat=zhat, v=v, want_S=True,
+                              below=True)
+    assert out["status"] == 0
+    S = out["S"].cpu().numpy()
+    assert np.array_equal(out["counts"].cpu().numpy(), np.sum(S <= u, axis=1))
+    assert np.array_equal(out["sizes"].cpu().numpy(), np.sum(S <= u, axis=0))
+    # oracle: the positive-set scan and calibration of the sign-reversed problem
+    r = oracle.krige(xo, yo, xp, yp, y_obs, 3, 0, 1.0, 0.1, 1.5, 0.01)
+    V = oracle.cov_matrix(x, y, 0, 1.0, 0.1, 1.5, diag_add=diag_add)
+    Lo, _ = oracle.potrf(V)
+    So = oracle.condition(oracle.trmm(Lo, Z), n_p, r["W"], y_obs)
+    assert rel(S, So) <= 1e-10
+    assert np.sum(np.abs(So - u) < 1e-9) == 0
+    t = (u - r["zhat"]) / np.sqrt(r["v"])
+    sc = oracle.scan(-So, -u, t)
+    assert np.array_equal(out["counts"].cpu().numpy(), sc["counts"])
+    np.testing.assert_allclose(out["psi"], sc["psi"], rtol=1e-9)
+    np.testing.assert_allclose(out["phi"], sc["phi"], rtol=1e-9)
+    cal = oracle.calibrate(sc["psi"], sc["phi"], t, c)
+    assert out["n_psi"] == cal["n_psi"] and out["n_phi"] == cal["n_phi"]
+    assert out["q_out"] == pytest.approx(cal["q_out"], rel=1e-9)
+    assert out["q_in"] == pytest.approx(cal["q_in"], rel=1e-9)
+    assert np.array_equal(out["cout"].cpu().numpy(), cal["cout"])
+    assert np.array_equal(out["cin"].cpu().numpy(), cal["cin"])
+    # bitwise against the positive-set call on the negated inputs
+    neg = g.excursion_regions(ctx, -M, n_p, n_o, nsim, -u, c, W=W, y_o=dev(-y_obs), zhat=-zhat, v=v)
+    assert neg["status"] == 0
+    for key in ("counts", "sizes", "cin", "cout"):
+        assert np.array_equal(neg[key].cpu().numpy(), out[key].cpu().numpy()), key
+    assert np.array_equal(neg["psi"], out["psi"]) and np.array_equal(neg["phi"], out["phi"])
+    assert neg["q_in"] == out["q_in"] and neg["q_out"] == out["q_out"]
+    A.close()
+
+
 def test_regions_error_paths(ctx):
     n_p, nsim = 50, 20
     M = dev_cm(np.full((n_p, nsim), -3.0))
