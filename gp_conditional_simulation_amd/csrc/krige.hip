@@ -19,17 +19,21 @@
 #include <vector>
 
 #include "common.h"
+#include "matern.h"
 
 namespace gpex {
 
 struct CovK {
     int kind;
     double sigma2, range, nu;
+    double h0, lcoef;   // Matern of another nu (matern.h)
 };
 
 __device__ __forceinline__ double covk(const CovK& p, double d) {
     if (p.kind == 1) return p.sigma2 * exp(-(d * d) / p.range);
-    double r = d / p.range, e = exp(-r);
+    double r = d / p.range;
+    if (!(p.nu == 0.5 || p.nu == 1.5 || p.nu == 2.5)) return p.sigma2 * matern_general(r, p.nu, p.h0, p.lcoef);
+    const double e = exp(-r);
     if (p.nu == 0.5) return p.sigma2 * e;
     if (p.nu == 1.5) return p.sigma2 * (1.0 + r) * e;
     return p.sigma2 * (1.0 + r + r * r / 3.0) * e;
@@ -209,7 +213,8 @@ extern "C" int gpex_krige(gpex_ctx_t ctx, const double* d_loc_o, int64_t n_o, co
     double* G = cv.get<double>(wsb, p_g);
     double* H = cv.get<double>(wsb, p_h);
     GemmTask* d_tk = cv.get<GemmTask>(wsb, p_tk);
-    CovK ck{params->kind, params->sigma2, params->range, params->nu};
+    CovK ck{params->kind, params->sigma2, params->range, params->nu, matern_h0(params->nu),
+            (1.0 - params->nu) * std::log(2.0) - std::lgamma(params->nu)};
     hipLaunchKernelGGL(k_cov_cross, dim3(nblk(n_o * n_p)), dim3(256), 0, s, d_loc_o, n_o, d_loc_p, n_p, ck, Vop);
     hipLaunchKernelGGL(k_design, dim3(nblk(rows_pad)), dim3(256), 0, s, d_loc_o, n_o, rows_pad, Xo, rows_pad);
     if (hipGetLastError() != hipSuccess) { cleanup(); return set_err(ctx, GPEX_ERR_HIP, "krige setup launch"); }

@@ -55,6 +55,8 @@ def lib():
         L.orc_trsm_lower_trans.argtypes = [_d, I64, I64, _d, I64, I64]
         L.orc_gemm.argtypes = [I, I, I64, I64, I64, D, _d, I64, _d, I64, D, _d, I64]
         L.orc_krige.restype = I64
+        L.orc_krige_mats.restype = I64
+        L.orc_krige_mats.argtypes = [_d, _d, _dv, _dv, I64, _dv, _dv, I64, _dv, I, D, _d, _dv, _dv, C.c_void_p]
         L.orc_krige.argtypes = [_dv, _dv, I64, _dv, _dv, I64, _dv, I, I, D, D, D, D, _d, _dv, _dv, C.c_void_p]
         L.orc_condition.argtypes = [_d, I64, I64, I64, I64, _d, _dv, _d, I64]
         L.orc_scan.argtypes = [_d, I64, I64, I64, C.c_void_p, D, _i64, _i32, C.c_void_p, C.c_void_p]
@@ -81,14 +83,44 @@ def _c(a):
     return np.ascontiguousarray(a, dtype=np.float64)
 
 
+def _half_integer(kind, nu) -> bool:
+    return kind != 0 or nu in (0.5, 1.5, 2.5)
+
+
+def matern_correlation(r, nu) -> np.ndarray:
+    """Matern correlation of any order nu ("Mixed-Precision GPU Acceleration for Confidence Regions
+    of Spatial Excursion Sets", Sec. V-E): 2^(1 - nu) / Gamma(nu) r^nu K_nu(r), 1 at r = 0, with
+    scipy's exponentially scaled K_nu (kve) and log-gamma as the library primitives:
+    exp((1 - nu) ln 2 - ln Gamma(nu) + nu ln r - r) kve(nu, r)."""
+    from scipy.special import gammaln, kve
+    r = np.asarray(r, dtype=np.float64)
+    out = np.ones_like(r)
+    pos = r > 0
+    rp = r[pos]
+    out[pos] = np.exp((1.0 - nu) * np.log(2.0) - gammaln(nu) + nu * np.log(rp) - rp) * kve(nu, rp)
+    return out
+
+
+def _general(d, sigma2, rng, nu):
+    return sigma2 * matern_correlation(np.asarray(d) / rng, nu)
+
+
 def cov(kind: int, sigma2: float, rng: float, nu: float, d: float) -> float:
-    """One covariance value (Matern half-integer nu with kind 0, Gaussian with kind 1)."""
+    """One covariance value (Matern with kind 0: half-integer nu in closed form in C, any other nu
+    by matern_correlation; Gaussian with kind 1)."""
+    if not _half_integer(kind, nu):
+        return float(_general(d, sigma2, rng, nu))
     return float(lib().orc_cov(kind, sigma2, rng, nu, d))
 
 
 def cov_matrix(x, y, kind, sigma2, rng, nu, nugget=0.0, diag_add=None) -> np.ndarray:
     x, y = _c(x), _c(y)
     n = len(x)
+    if not _half_integer(kind, nu):
+        d = np.hypot(x[:, None] - x[None, :], y[:, None] - y[None, :])
+        V = np.asfortranarray(_general(d, sigma2, rng, nu))
+        V[np.diag_indices(n)] += _c(diag_add) if diag_add is not None else nugget
+        return V
     V = np.empty((n, n), order="F")
     da = None
     if diag_add is not None:
@@ -100,6 +132,9 @@ def cov_matrix(x, y, kind, sigma2, rng, nu, nugget=0.0, diag_add=None) -> np.nda
 
 def cov_cross(xa, ya, xb, yb, kind, sigma2, rng, nu) -> np.ndarray:
     xa, ya, xb, yb = _c(xa), _c(ya), _c(xb), _c(yb)
+    if not _half_integer(kind, nu):
+        d = np.hypot(xa[:, None] - xb[None, :], ya[:, None] - yb[None, :])
+        return np.asfortranarray(_general(d, sigma2, rng, nu))
     Cm = np.empty((len(xa), len(xb)), order="F")
     lib().orc_cov_cross(xa, ya, len(xa), xb, yb, len(xb), kind, sigma2, rng, nu, Cm, len(xa))
     return Cm
@@ -166,8 +201,15 @@ def krige(xo, yo, xp, yp, y_obs, k_trend, kind, sigma2, rng, nu, tau2, want_H=Fa
     zhat = np.zeros(n_p)
     v = np.zeros(n_p)
     H = np.zeros((max(k_trend, 1), n_p), order="F") if want_H else None
-    info = lib().orc_krige(xo, yo, n_o, xp, yp, n_p, y_obs, k_trend, kind, sigma2, rng, nu, tau2,
-                           W, zhat, v, H.ctypes.data if H is not None else None)
+    if not _half_integer(kind, nu):
+        # covariances of the general Matern order here, the kriging algebra in C as for the others
+        Sy = cov_matrix(xo, yo, kind, sigma2, rng, nu, nugget=tau2)
+        Vop = cov_cross(xo, yo, xp, yp, kind, sigma2, rng, nu)
+        info = lib().orc_krige_mats(Sy, Vop, xo, yo, n_o, xp, yp, n_p, y_obs, k_trend, sigma2, W, zhat, v,
+                                    H.ctypes.data if H is not None else None)
+    else:
+        info = lib().orc_krige(xo, yo, n_o, xp, yp, n_p, y_obs, k_trend, kind, sigma2, rng, nu, tau2,
+                               W, zhat, v, H.ctypes.data if H is not None else None)
     out = {"W": W, "zhat": zhat, "v": v, "info": int(info)}
     if want_H:
         out["H"] = H[:k_trend]

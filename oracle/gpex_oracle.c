@@ -211,19 +211,16 @@ void orc_gemm(int transa, int transb, int64_t m, int64_t n, int64_t k, double al
 /* Outputs: W (n_o x n_p, ld n_o), zhat (n_p), v (n_p); H (k x n_p) if H_out is given.        */
 /* Returns 0; the 1-based failing column of Sigma_y's factor; or -1 if G is not SPD.          */
 /* ------------------------------------------------------------------------------------------ */
-int64_t orc_krige(const double* xo, const double* yo, int64_t n_o, const double* xp,
-                  const double* yp, int64_t n_p, const double* y_obs, int k_trend, int kind,
-                  double sigma2, double range, double nu, double tau2, double* W, double* zhat,
-                  double* v, double* H_out) {
+/* orc_krige_mats: the same from given Sigma_y (n_o x n_o, ld n_o) and V_op (n_o x n_p, ld n_o),
+ * which it does not modify; orc_krige builds them from the locations with orc_cov. */
+int64_t orc_krige_mats(const double* Sy, const double* Vop, const double* xo, const double* yo, int64_t n_o,
+                       const double* xp, const double* yp, int64_t n_p, const double* y_obs, int k_trend,
+                       double sigma2, double* W, double* zhat, double* v, double* H_out) {
     size_t no = (size_t)n_o, np_ = (size_t)n_p;
-    double* Sy = (double*)malloc(sizeof(double) * no * no);
     double* Lo = (double*)malloc(sizeof(double) * no * no);
-    double* Vop = (double*)malloc(sizeof(double) * no * np_);
     double* U = (double*)malloc(sizeof(double) * no * np_);
     int64_t info = 0;
-    orc_cov_matrix(xo, yo, n_o, kind, sigma2, range, nu, tau2, NULL, Sy, n_o);
     memcpy(Lo, Sy, sizeof(double) * no * no);
-    orc_cov_cross(xo, yo, n_o, xp, yp, n_p, kind, sigma2, range, nu, Vop, n_o);
     info = orc_potrf(Lo, n_o, n_o);
     if (info != 0) goto done;
     /* Right-hand side of the weight solves: V_op - X_o H (or V_op without a trend). */
@@ -279,7 +276,20 @@ int64_t orc_krige(const double* xo, const double* yo, int64_t n_o, const double*
         v[j] = sigma2 + wu - 2.0 * cw;
     }
 done:
-    free(Sy); free(Lo); free(Vop); free(U);
+    free(Lo); free(U);
+    return info;
+}
+
+int64_t orc_krige(const double* xo, const double* yo, int64_t n_o, const double* xp,
+                  const double* yp, int64_t n_p, const double* y_obs, int k_trend, int kind,
+                  double sigma2, double range, double nu, double tau2, double* W, double* zhat,
+                  double* v, double* H_out) {
+    double* Sy = (double*)malloc(sizeof(double) * (size_t)n_o * (size_t)n_o);
+    double* Vop = (double*)malloc(sizeof(double) * (size_t)n_o * (size_t)n_p);
+    orc_cov_matrix(xo, yo, n_o, kind, sigma2, range, nu, tau2, NULL, Sy, n_o);
+    orc_cov_cross(xo, yo, n_o, xp, yp, n_p, kind, sigma2, range, nu, Vop, n_o);
+    int64_t info = orc_krige_mats(Sy, Vop, xo, yo, n_o, xp, yp, n_p, y_obs, k_trend, sigma2, W, zhat, v, H_out);
+    free(Sy); free(Vop);
     return info;
 }
 

@@ -106,6 +106,59 @@ def test_cov_gen_extreme_ranges(ctx, kind, nu, beta):
         assert tiny.size > 0   # the case reaches subnormal entries
 
 
+@pytest.mark.parametrize("nu", [0.3, 0.75, 1.0, 2.2, 6.0])
+@pytest.mark.parametrize("beta", [0.1, 0.01])
+def test_cov_gen_general_matern_order(ctx, nu, beta):
+    """Matern of an order without a closed form (the trapezoidal K_nu of the generator) against the
+    oracle's scipy-based 2^(1-nu)/Gamma(nu) r^nu K_nu(r): both carry a few ulps of rounding in r and
+    in exp's argument (about r + nu |ln r| ulps) and scipy's K_nu about 1e-14."""
+    n, nb, sigma2 = 700, 128, 1.7
+    x, y = syn.uniform_locations(n, 31)
+    x, y, _ = syn.ordered_locations(x, y)
+    params = {"kind": 0, "sigma2": sigma2, "range": beta, "nu": nu, "nugget": 1e-4}
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=0)
+    V = oracle.cov_matrix(x, y, 0, sigma2, beta, nu, nugget=1e-4)
+    Vg = A.to_dense().cpu().numpy()
+    st_g = A.stats()
+    A.close()
+    low = np.tril_indices(n)
+    r = np.hypot(x[:, None] - x[None, :], y[:, None] - y[None, :])[low] / beta
+    lr = np.abs(np.log(np.where(r > 0, r, 1.0)))
+    err = np.abs(Vg[low] - V[low])
+    bound = 1e-300 + (1e-13 + 8 * np.finfo(float).eps * (r + nu * lr)) * np.abs(V[low])
+    assert np.all(err <= bound), float(np.max(err / bound))
+    np.testing.assert_allclose(st_g[:, 0], oracle.tile_stats(V, nb)[:, 0], rtol=1e-12)
+
+
+def test_general_matern_order_factor_simulation_and_kriging(ctx):
+    """nu = 0.8 through the rest of the path: the FP64 factor and M = L Z against the oracle's, and
+    universal kriging against the oracle's (its covariances from scipy, its algebra the same C code
+    as for the closed forms).  The matrices agree to about 1e-14, so the factor and the kriging
+    weights agree to that times the conditioning (nugget 1e-4)."""
+    n, nb, nsim, nu = 1100, 128, 40, 0.8
+    x, y = syn.uniform_locations(n, 33)
+    x, y, _ = syn.ordered_locations(x, y)
+    params = {"kind": 0, "sigma2": 1.0, "range": 0.15, "nu": nu, "nugget": 1e-4}
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=0)
+    assert g.potrf_mp(ctx, A) == 0
+    Z = syn.explicit_normals(n, nsim, 2021)
+    M, _ = g.trmm_sim(ctx, A, nsim, Z=dev_cm(Z))
+    Lo, info = oracle.potrf(oracle.cov_matrix(x, y, 0, 1.0, 0.15, nu, nugget=1e-4))
+    assert info == 0
+    assert rel(A.to_dense().cpu().numpy(), Lo) <= 1e-8
+    assert rel(M.cpu().numpy(), oracle.trmm(Lo, Z)) <= 1e-8
+    A.close()
+    xo, yo, xp, yp, y_obs = _krige_case(900, 300, 8)
+    kp = {"kind": 0, "sigma2": 1.0, "range": 0.1, "nu": nu}
+    W, zhat, v, info = g.krige(ctx, dev(np.r_[xo, yo]), 900, dev(np.r_[xp, yp]), 300, dev(y_obs), 3, kp, 0.01, 128)
+    assert info == 0
+    r = oracle.krige(xo, yo, xp, yp, y_obs, 3, 0, 1.0, 0.1, nu, 0.01)
+    assert r["info"] == 0
+    assert rel(W.cpu().numpy(), r["W"]) <= 1e-8
+    assert rel(zhat.cpu().numpy(), r["zhat"]) <= 1e-8
+    assert rel(v.cpu().numpy(), r["v"]) <= 1e-8
+
+
 @pytest.mark.parametrize("tol", [1e-9, 1e-6, 1e-3])
 def test_plan_from_device_stats_matches_oracle_plan(ctx, tol):
     n, nb = 3000, 160

@@ -56,7 +56,52 @@ def test_gaussian_correlation_special_values():
     assert oracle.cov(1, s2, theta, 0.0, 0.0) == s2
     assert oracle.cov(1, s2, theta, 0.0, math.sqrt(theta)) == pytest.approx(s2 / math.e, rel=1e-15)
     assert oracle.cov(1, s2, theta, 0.0, 2 * math.sqrt(theta)) == pytest.approx(s2 * math.exp(-4), rel=1e-14)
-    assert math.isnan(oracle.cov(0, 1.0, 0.1, 0.75, 0.3))  # unsupported nu
+    assert math.isnan(oracle.lib().orc_cov(0, 1.0, 0.1, 0.75, 0.3))  # the C closed forms: half-integer nu only
+
+
+@pytest.mark.parametrize("nu", [0.5, 1.5, 2.5])
+def test_general_matern_equals_closed_forms(nu):
+    # the general-order route (scipy kve) at the half-integer orders the C oracle has in closed form
+    r = np.concatenate([[0.0, 1e-12, 1e-6], np.geomspace(1e-3, 700, 200)])
+    got = oracle.matern_correlation(r, nu)
+    ref = np.array([oracle.lib().orc_cov(0, 1.0, 1.0, nu, x) for x in r])
+    # both sides round exp's argument (about r ulps at large r)
+    assert np.all(np.abs(got - ref) <= (2e-14 + 8 * np.finfo(float).eps * r) * ref + 1e-300)
+
+
+def test_general_matern_matches_high_precision_bessel():
+    # against 30-digit mpmath values of 2^(1-nu)/Gamma(nu) r^nu K_nu(r) (an independent library)
+    mp = pytest.importorskip("mpmath")
+    mp.mp.dps = 30
+    for nu in (0.05, 0.3, 0.75, 1.0, 2.2, 3.7, 6.0, 8.0):
+        for r in (1e-7, 1e-3, 0.2, 1.0, 3.3, 17.0, 90.0, 400.0):
+            ref = float(mp.mpf(2) ** (1 - nu) / mp.gamma(nu) * mp.mpf(r) ** nu * mp.besselk(nu, r))
+            got = float(oracle.matern_correlation(np.array([r]), nu)[0])
+            assert got == pytest.approx(ref, rel=1e-13 + 8 * np.finfo(float).eps * r), (nu, r)
+    # limits: 1 at r = 0 and decreasing in r
+    r = np.geomspace(1e-2, 50, 400)
+    for nu in (0.3, 1.0, 4.0):
+        c = oracle.matern_correlation(np.r_[0.0, 1e-9, r], nu)
+        assert c[0] == 1.0 and abs(c[1] - 1.0) < 1e-4 and np.all(np.diff(c[2:]) < 0)
+
+
+def test_krige_from_matrices_equals_krige():
+    # the kriging algebra on given Sigma_y and V_op (the general-order route) is the same C code as
+    # the location-based call: bitwise equal at a closed-form order
+    rng = np.random.default_rng(5)
+    xo, yo, xp, yp = rng.random(60), rng.random(60), rng.random(25), rng.random(25)
+    y_obs = rng.standard_normal(60)
+    ref = oracle.krige(xo, yo, xp, yp, y_obs, 3, 0, 1.1, 0.2, 1.5, 0.02)
+    Sy = oracle.cov_matrix(xo, yo, 0, 1.1, 0.2, 1.5, nugget=0.02)
+    Vop = oracle.cov_cross(xo, yo, xp, yp, 0, 1.1, 0.2, 1.5)
+    W = np.zeros((60, 25), order="F"); z = np.zeros(25); v = np.zeros(25)
+    info = oracle.lib().orc_krige_mats(Sy, Vop, xo, yo, 60, xp, yp, 25, y_obs, 3, 1.1, W, z, v, None)
+    assert info == 0
+    assert np.array_equal(W, ref["W"]) and np.array_equal(z, ref["zhat"]) and np.array_equal(v, ref["v"])
+    # a general order goes through it: unbiasedness X_o^T W = X_p^T holds
+    g = oracle.krige(xo, yo, xp, yp, y_obs, 3, 0, 1.1, 0.2, 0.8, 0.02)
+    assert g["info"] == 0
+    np.testing.assert_allclose(np.c_[np.ones(60), xo, yo].T @ g["W"], np.c_[np.ones(25), xp, yp].T, atol=1e-10)
 
 
 def test_cov_matrix_matches_library_distance_and_bessel():
