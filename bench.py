@@ -35,8 +35,9 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def tile_flops(pmap, nt, nb, nsim, amp):
-    """Algorithmic flops per compute precision of the tiled Cholesky + TRMM (tiles of nb)."""
+def tile_flops(pmap, nt, nb, nsim, amp, diag16=False):
+    """Algorithmic flops per compute precision of the tiled Cholesky + TRMM (tiles of nb); diag16:
+    the TRMM's diagonal tiles ran on FP16 matrix cores (as two FP16 parts) instead of FP32."""
     f = {"fp64": 0.0, "fp32": 0.0, "fp16": 0.0}
     name = {0: "fp64", 1: "fp32", 2: "fp16"}
     nb3 = float(nb) ** 3
@@ -49,7 +50,7 @@ def tile_flops(pmap, nt, nb, nsim, amp):
                 f[name[int(pmap[i, j])]] += 2.0 * nb3            # GEMM in the output tile's precision
     nb2s = float(nb) * nb * nsim
     if amp:
-        f["fp32"] += nt * nb2s                                   # diagonal TRMM tiles in FP32
+        f["fp16" if diag16 else "fp32"] += nt * nb2s             # diagonal TRMM tiles
         f["fp16"] += nt * (nt - 1) / 2 * 2.0 * nb2s              # off-diagonal tiles in FP16
     else:
         f["fp64"] += nt * nb2s + nt * (nt - 1) * nb2s
@@ -126,8 +127,8 @@ def trmm_sweep(args):
     pages' single-node TRMM figure ("Mixed-Precision GPU Acceleration for Confidence Regions of
     Spatial Excursion Sets", Fig. 6): N uniform locations (Morton order), Matern nu = 1/2,
     sigma^2 = 1, nugget 1e-4, range 0.033 / 0.1 / 0.234, tile 1024, tolerance 1e-8, nsim columns.
-    The factor is computed once per point; the TRMM (seeded normals, B = Z/s in FP16, FP32
-    diagonal, FP16 off-diagonal, FP64 output) is timed over three runs after a warm-up.  Reported
+    The factor is computed once per point; the TRMM (seeded normals, B = Z/s in FP16, diagonal at
+    about FP32 accuracy, FP16 off-diagonal, FP64 output) is timed over three runs after a warm-up.  Reported
     as N^2 nsim / T and as a multiple of the FP64 matrix-core peak."""
     import numpy as np
     import torch
@@ -506,14 +507,20 @@ def main():
     per_launch_flops = lib["update_flops_exact"][prec] / launches
     achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
     busy_rate = lib["update_flops_exact"][prec] / (busy_ms * 1e-3) / 1e12
-    tf = tile_flops(info["map"], info["nt"], info["nb"], nsim, w.amp)
+    with_diag = all(r["lib"]["trmm_rows_with_diagonal"] for r in recs)
+    tf = tile_flops(info["map"], info["nt"], info["nb"], nsim, w.amp, diag16=with_diag)
     t_ideal = sum(tf[p] / (PEAK_TF[p] * 1e12) for p in tf)
     tiles = last["diag"]["tiles"]
     fac = "+".join(p for p, c in zip(("f64", "f32", "f16"), tiles) if c) or "f64"
-    dtype = f"{fac} factor tiles + {'f16 TRMM (f32 diagonal, f32 accumulation)' if w.amp else 'f64 TRMM'}"
+    trmm_kind = ("f16 TRMM (diagonal as two f16 parts, f32 accumulation)" if with_diag else
+                 "f16 TRMM (f32 diagonal, f32 accumulation)") if w.amp else "f64 TRMM"
+    dtype = f"{fac} factor tiles + {trmm_kind}"
     trmm_rows_ms = statistics.median(r["lib"]["trmm_rows_ms"] for r in recs)
     nt_, nb_ = info["nt"], info["nb"]
-    rows_flops = 2.0 * nb_ * nb_ * (nt_ * (nt_ - 1) / 2) * (((nsim + 127) // 128) * 128)
+    # algorithmic flops of the launch on the padded columns: 2 nb^2 per off-diagonal tile and
+    # column, nb^2 per (triangular) diagonal tile when the launch applies those too
+    cols_ = ((nsim + 127) // 128) * 128
+    rows_flops = (2.0 * (nt_ * (nt_ - 1) / 2) + (nt_ if with_diag else 0)) * nb_ * nb_ * cols_
     res = {
         "metric": "POTRF+TRMM FP64-equiv Tflop/s and conditional sims/sec at N=100k, 1 MI355X",
         "value": round(value, 3),
@@ -550,7 +557,8 @@ def main():
                                       "tile rows (unpadded)",
                      "busy_ms": round(busy_ms, 2), "busy_rate_tflops": round(busy_rate, 2),
                      "busy_frac": round(busy_rate / PEAK_TF[prec], 4)},
-        "simulation_product": {"kernel": "FP16 row-panel launch of the TRMM (off-diagonal tiles)",
+        "simulation_product": {"kernel": "FP16 row-panel launch of the TRMM (off-diagonal tiles"
+                                         + (" and the diagonal tiles' two FP16 parts)" if with_diag else ")"),
                                "ms": round(trmm_rows_ms, 3), "flops": float(f"{rows_flops:.4e}"),
                                "tflops": round(rows_flops / (trmm_rows_ms * 1e-3) / 1e12, 1) if trmm_rows_ms else None,
                                "frac_fp16_peak": round(rows_flops / (trmm_rows_ms * 1e-3) / 1e12 / PEAK_TF["fp16"], 4)
@@ -602,7 +610,8 @@ def mp_workload(args, name, ctx, loc, M):
     T_potrf = statistics.median(r["potrf"] for r in recs)
     T_trmm = statistics.median(r["trmm"] for r in recs)
     last = recs[-1]
-    tf = tile_flops(last["info"]["map"], last["info"]["nt"], last["info"]["nb"], w.nsim, w.amp)
+    tf = tile_flops(last["info"]["map"], last["info"]["nt"], last["info"]["nb"], w.nsim, w.amp,
+                    diag16=all(r["lib"]["trmm_rows_with_diagonal"] for r in recs))
     t_ideal = sum(tf[p] / (PEAK_TF[p] * 1e12) for p in tf)
     upd = {}
     for p in ("fp64", "fp32", "fp16"):

@@ -212,7 +212,8 @@ class Context:
                 "update_flops": {"fp64": v[3], "fp32": v[6], "fp16": v[9]},
                 "update_flops_exact": {"fp64": v[12], "fp32": v[13], "fp16": v[14]},
                 "update_busy_ms": {"fp64": v[15], "fp32": v[16], "fp16": v[17]},
-                "trmm_ms": v[10], "trmm_kernels_ms": v[11], "trmm_rows_ms": v[18]}
+                "trmm_ms": v[10], "trmm_kernels_ms": v[11], "trmm_rows_ms": v[18],
+                "trmm_rows_with_diagonal": bool(v[19])}
 
 
 @dataclasses.dataclass
@@ -252,11 +253,12 @@ class Tiled:
         self.ctx.check(lib().gpex_tiled_block(self.ctx.h, self.h, r0, c0, rows, cols, _cm(out), rows))
         return out
 
-    def block_raw(self, r0: int, c0: int, rows: int, cols: int, fp16_copy: bool = False):
-        """Stored values (or the FP16 copy of the factor) of a block, exactly, without unscaling."""
+    def block_raw(self, r0: int, c0: int, rows: int, cols: int, fp16_copy: bool = False, diag_parts: bool = False):
+        """Stored values of a block, exactly, without unscaling; fp16_copy: the FP16 copy of the
+        off-diagonal factor tiles; diag_parts: the diagonal tiles as the sum of their two FP16 parts."""
+        which = 2 if diag_parts else int(fp16_copy)
         out = colmajor(rows, cols, self.ctx)
-        self.ctx.check(lib().gpex_tiled_block_raw(self.ctx.h, self.h, int(fp16_copy), r0, c0, rows, cols, _cm(out),
-                                                  rows))
+        self.ctx.check(lib().gpex_tiled_block_raw(self.ctx.h, self.h, which, r0, c0, rows, cols, _cm(out), rows))
         return out
 
     def close(self):

@@ -233,6 +233,43 @@ __global__ void k_join(const double* ws, double* A, int64_t lda, double* T, int6
     }
 }
 
+// The diagonal tiles of the factor as two FP16 parts each, for the simulation product: row r of
+// tile k goes to row r of FP16 row panel k (leading dimension (k + 2) nb), hi = cast16(L) and
+// lo = cast16(L - hi), zeros above the diagonal, in pairs of w-wide slabs from column k nb
+// (w = l16_pair_w(nb): column c's hi at k nb + 2 w (c / w) + c % w, its lo w further).  hi + lo
+// carries L to about 22 bits (an FP32 copy: 24), and the simulation product takes both on its
+// FP16 matrix cores against the same rows of Z / s.  One workgroup per 64 x 64 part of a tile
+// (blockIdx.z = k), through LDS: column-major reads, row-major writes.
+constexpr int D16_T = 64;
+__global__ __launch_bounds__(256) void k_diag16(const uint8_t* const* tiles, int nb, _Float16* l16,
+                                                unsigned long long* flags) {
+    __shared__ double t[D16_T][D16_T + 1];
+    const int k = blockIdx.z, r0 = blockIdx.y * D16_T, c0 = blockIdx.x * D16_T;
+    const double* L = reinterpret_cast<const double*>(tiles[k]);
+    const int tx = threadIdx.x % D16_T, ty = threadIdx.x / D16_T;
+    for (int c = ty; c < D16_T; c += 4) {   // t[row][col], column-major reads
+        const int gr = r0 + tx, gc = c0 + c;
+        t[tx][c] = (gr < nb && gc < nb && gc <= gr) ? L[gr + (int64_t)gc * nb] : 0.0;
+    }
+    __syncthreads();
+    const int64_t ld = (int64_t)(k + 2) * nb;
+    _Float16* panel = l16 + (size_t)nb * nb * (size_t)((int64_t)k * (k - 1) / 2 + 2 * (int64_t)k);
+    const int w = l16_pair_w(nb);
+    bool ovf = false;
+    for (int r = ty; r < D16_T; r += 4) {   // row-major writes
+        const int gr = r0 + r, gc = c0 + tx;
+        if (gr >= nb || gc >= nb) continue;
+        const double v = t[r][tx];
+        const _Float16 hi = f64_to_f16(v);
+        const _Float16 lo = f64_to_f16(v - (double)hi);
+        if (__builtin_isinf((float)hi) && !__builtin_isinf(v)) ovf = true;
+        _Float16* at = panel + gr * ld + (int64_t)k * nb + 2 * w * (gc / w) + gc % w;
+        at[0] = hi;
+        at[w] = lo;
+    }
+    if (ovf && flags) atomicOr(&flags[FLAG_FP16_OVF], 1ull);
+}
+
 // Size of the first half when a diagonal block of order n > LEAF is split: whole leaves first
 // (a multiple of LEAF, half of ceil(n / LEAF) leaves), so the recursion ends in the fewest leaves
 // ceil(n / LEAF) and the fewest halving steps; orders that are multiples of 2 LEAF halve exactly.
@@ -328,10 +365,10 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     hipStream_t s = ctx->stream;
     if (!a->tinv)
         GPEX_TRY(tiled_alloc(ctx, a, (void**)&a->tinv, sizeof(double) * tile_el * nt, "inverse diagonal tiles"));
-    // FP16 copy of the off-diagonal factor for the simulation product, written by the panel solves
+    // FP16 copy of the factor for the simulation product: off-diagonal tiles written by the panel
+    // solves, the two FP16 parts of the diagonal tiles once the factorization is done
     if (a->opts.amp && nt > 1 && !a->l16)
-        GPEX_TRY(tiled_alloc(ctx, a, (void**)&a->l16, sizeof(_Float16) * tile_el * (size_t)(nt * (nt - 1) / 2),
-                             "FP16 factor panels"));
+        GPEX_TRY(tiled_alloc(ctx, a, (void**)&a->l16, sizeof(_Float16) * a->l16_elems(), "FP16 factor panels"));
     // rows of tile row i that exist (the last one may be padding beyond n)
     auto rows = [&](int64_t i) { return (double)std::min<int64_t>(nb, a->n - i * nb); };
     // FP64 tiles still hold V (the generator scaled only the reduced-precision tiles): step 0 applies
@@ -387,6 +424,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     size_t ntask = 0;
     for (int64_t k = 0; k < nt; ++k) ntask += (size_t)(nt - k - 1) + (size_t)(nt - k - 1) * (nt - k) / 2;
     const size_t p_tasks = cv.add(sizeof(GemmTask) * ntask), p_copies = cv.add(sizeof(CopyTask) * (size_t)(nt * (nt - 1) / 2));
+    const size_t p_dtiles = cv.add(a->l16 ? sizeof(void*) * (size_t)nt : 0);
     void* wsb = nullptr;
     GPEX_TRY(ws_get(ctx, WS_POTRF, cv.total, &wsb, "factorization workspace"));
     uint8_t* pws = cv.get<uint8_t>(wsb, p_pws);
@@ -405,6 +443,10 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     };
     GemmTask* d_tasks = cv.get<GemmTask>(wsb, p_tasks);
     CopyTask* d_copies = cv.get<CopyTask>(wsb, p_copies);
+    const uint8_t** d_diag_tiles = cv.get<const uint8_t*>(wsb, p_dtiles);
+    std::vector<const uint8_t*> diag_tiles;
+    if (a->l16)
+        for (int64_t k = 0; k < nt; ++k) diag_tiles.push_back(static_cast<const uint8_t*>(a->tile(k, k)));
     tasks.reserve(ntask);
     copies.reserve((size_t)(nt * (nt - 1) / 2));
     for (int64_t k = 0; k < nt; ++k) {
@@ -430,7 +472,7 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
             g.tri = TRI_B_UPPER;   // T_kk^T is upper triangular
             if (a->l16) {   // tile (i, k) lands at columns [k nb, (k+1) nb) of row panel i
                 g.C2 = a->l16_panel(i) + (size_t)k * nb;
-                g.ldc2 = i * nb;
+                g.ldc2 = a->l16_ld(i);
             }
             if (need32[(size_t)(i * nt + k)]) g.C3 = copy32(i, k);
             if (need64[(size_t)(i * nt + k)]) g.C4 = copy64(i, k);
@@ -442,8 +484,8 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
                 GemmTask g{};
                 if (p == DT_F16 && l16_ops) {
                     // op(A)[r, c] = L_ik[r, c] and op(B)[c, r'] = L_jk[r', c], both k-contiguous
-                    g.A = a->l16_panel(i) + (size_t)k * nb; g.lda = i * nb; g.ta = DT_F16; g.transA = 1;
-                    g.B = a->l16_panel(j) + (size_t)k * nb; g.ldb = j * nb; g.tb = DT_F16; g.transB = 0;
+                    g.A = a->l16_panel(i) + (size_t)k * nb; g.lda = a->l16_ld(i); g.ta = DT_F16; g.transA = 1;
+                    g.B = a->l16_panel(j) + (size_t)k * nb; g.ldb = a->l16_ld(j); g.tb = DT_F16; g.transB = 0;
                 } else {
                     operand(i, k, p, g.A, g.ta);
                     operand(j, k, p, g.B, g.tb);
@@ -480,6 +522,8 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
     // vectors stay alive until the final synchronisation
     if (!tasks.empty()) GPEX_HIP(ctx, hipMemcpyAsync(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice, s));
     if (!copies.empty()) GPEX_HIP(ctx, hipMemcpyAsync(d_copies, copies.data(), sizeof(CopyTask) * copies.size(), hipMemcpyHostToDevice, s));
+    if (!diag_tiles.empty())
+        GPEX_HIP(ctx, hipMemcpyAsync(d_diag_tiles, diag_tiles.data(), sizeof(void*) * diag_tiles.size(), hipMemcpyHostToDevice, s));
     GPEX_HIP(ctx, hipMemsetAsync(ctx->d_flags + FLAG_INFO, 0, sizeof(long long) * (FLAG_BADTASK + 1), s));
 
     Timer tm{ctx, {}, 0};
@@ -568,6 +612,12 @@ extern "C" int gpex_potrf_mp(gpex_ctx_t ctx, gpex_tiled_t a, int64_t* info) {
         }
         // join: the context stream waits for the last bulk update
         if (nt > 1) GPEX_TRY(wait(s, evr[(size_t)nt - 2]));
+        if (a->l16) {   // the diagonal tiles' two FP16 parts, beside their off-diagonal rows
+            const unsigned nsub = (unsigned)((nb + D16_T - 1) / D16_T);
+            hipLaunchKernelGGL(k_diag16, dim3(nsub, nsub, (unsigned)nt), dim3(256), 0, s, d_diag_tiles, nb, a->l16,
+                               reinterpret_cast<unsigned long long*>(ctx->d_flags));
+            GPEX_HIP(ctx, hipGetLastError());
+        }
         return GPEX_OK;
     };
     int r = schedule();

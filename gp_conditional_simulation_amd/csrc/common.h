@@ -68,11 +68,17 @@ struct gpex_tiled_s {
     double s = 1.0;
     std::vector<double> stats;       // 3 per lower tile: sum of squares, min, max (unscaled)
     double* tinv = nullptr;          // nt tiles nb x nb FP64: inverse of each diagonal factor tile
-    // FP16 copy of the off-diagonal factor for the simulation product and the factorization's FP16
-    // updates (amp only): tile row i as one row-major panel of nb x (i nb) at l16 + nb*nb*i(i-1)/2
-    // (k contiguous, leading dim i nb)
+    // FP16 copy of the factor for the simulation product and the factorization's FP16 updates (amp
+    // only, more than one tile row): tile row i as one row-major panel of nb x ((i + 2) nb), k
+    // contiguous, at l16 + nb*nb*(i(i-1)/2 + 2i): columns [0, i nb) hold cast16 of the off-diagonal
+    // tiles (i, 0..i-1), columns [i nb, (i+2) nb) the diagonal tile L_ii as two FP16 parts
+    // (hi = cast16(L_ii), lo = cast16(L_ii - hi), zeros above the diagonal) in pairs of w-wide
+    // slabs, w = l16_pair_w(nb): column c of L_ii has hi at i nb + 2 w (c / w) + c % w and lo w
+    // further.
     _Float16* l16 = nullptr;
-    _Float16* l16_panel(int64_t i) const { return l16 + (size_t)nb * nb * (size_t)(i * (i - 1) / 2); }
+    _Float16* l16_panel(int64_t i) const { return l16 + (size_t)nb * nb * (size_t)(i * (i - 1) / 2 + 2 * i); }
+    int64_t l16_ld(int64_t i) const { return (i + 2) * (int64_t)nb; }
+    size_t l16_elems() const { return (size_t)nb * nb * (size_t)(nt * (nt - 1) / 2 + 2 * nt); }
     bool factored = false;
     bool failed = false;             // a factorization stopped at a non-positive pivot: tiles hold garbage
     // FP64 tiles hold V rather than s^2 V (reduced tiles hold s^2 V): the factorization applies s^2
@@ -116,6 +122,10 @@ int ws_get(gpex_ctx_t ctx, int slot, size_t bytes, void** out, const char* what)
 inline size_t al256(size_t b) { return (b + 255) / 256 * 256; }
 // Consecutive 256-byte aligned pieces of one workspace buffer: size them with add(), then take
 // them in the same order from the buffer.
+// Slab width of the diagonal tiles' (hi, lo) pairs in the FP16 factor panels: 64 (the row-panel
+// kernel's k slab) when it divides the tile order, else the whole tile (one pair).
+__host__ __device__ inline int l16_pair_w(int nb) { return nb % 64 == 0 ? 64 : nb; }
+
 struct Carve {
     size_t total = 0;
     std::vector<size_t> at;
@@ -169,7 +179,11 @@ struct GemmTask {
     // of the task's C (the tile padding beyond them is computed but not stored, and C is read
     // only inside it).  0: all of C.
     int32_t m_store, n_store;
-    int32_t pad3;
+    // Row panels of the simulation product only (the 256 x 256 FP16 kernel): the last 2 kdup values
+    // of k are the diagonal tile (order kdup) as pairs of 64-wide slabs (hi, lo), both meeting the
+    // same 64 rows of B: k = K - 2 kdup + 128 s + 64 h + t (h = 0, 1; t < 64) reads B row
+    // K - 2 kdup + 64 s + t.  0: off.
+    int32_t kdup;
 };
 
 // Triangular structure of a task.  TRI_C_LOWER: only the lower triangle of C is wanted (blocks
@@ -196,6 +210,11 @@ int gemm_launch(gpex_ctx_t ctx, hipStream_t s, int compute, const GemmTask* d_ta
 int gemm1(gpex_ctx_t ctx, int compute, const void* A, int ta, int transA, int64_t lda,
           const void* B, int tb, int transB, int64_t ldb, void* C, int tc, int64_t ldc, int M,
           int N, int K, double alpha, double beta);
+
+// Whether the 256 x 256 FP16 row-panel kernel takes a launch of these tasks (the shape and
+// alignment it needs, at least 1024 workgroups, the kernel enabled), and its launch.
+bool panel16_takes(const GemmTask& one, int ntasks);
+int panel16_launch(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one);
 
 // ---- small helpers (chol.hip) ---------------------------------------------------------------
 // Dense 2-D copy with element-type conversion (RNE on narrowing; FP16 overflow sets the flag).

@@ -300,7 +300,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
         __builtin_memcpy(&T, w, sizeof(GemmTask));
     }
     if (!type_ok<TA>(T.ta) || !type_ok<TB>(T.tb) || !type_ok<TC>(T.tc) || T.transA != TRA ||
-        (T.transB != 0) != (TRB != 0)) {
+        (T.transB != 0) != (TRB != 0) || T.kdup != 0) {
         if (threadIdx.x == 0 && flags) atomicOr(&flags[FLAG_BADTASK], 1ull);
         return;
     }
@@ -597,8 +597,7 @@ static int try_typed(hipStream_t s, const GemmTask* d_tasks, int ntasks, const G
         // row panels of the simulation product: 256 x 256 blocks (panel16.h) when the part is all
         // of C and that still leaves at least 1024 workgroups
         const bool whole = p.fast && p.m_off == 0 && p.n_off == 0 && p.bmc * BM == one.M && p.bnc * BN == one.N;
-        if (g_panel16 && whole && panel16_fits(one) &&
-            (int64_t)ntasks * (one.M / P16_BM) * (one.N / P16_BN) >= 1024) {
+        if (whole && panel16_takes(one, ntasks)) {
             const Part w{0, 0, one.M / P16_BM, one.N / P16_BN, true};
             hipLaunchKernelGGL(k_panel16<0>, dim3((unsigned)part_grid(w, ntasks, xcd)), dim3(P16_THR), 0, s, d_tasks,
                                ntasks, w.bmc, w.bnc, xcd, fl);

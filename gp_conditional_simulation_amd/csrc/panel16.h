@@ -2,7 +2,10 @@
 // C (FP64, column-major) = alpha A B + beta C with A a row-major FP16 factor panel (M x K, lda) and
 // B = Z / s in FP16 (column-major K x N, ldb): the GEMM16 tasks of one tile row of L summed as one
 // product ("Mixed-Precision GPU Acceleration for Confidence Regions of Spatial Excursion Sets",
-// Algorithm 1).  Included by gemm_kernel.h (fragment types, matrix-core wrappers, GemmTask).
+// Algorithm 1).  A task may carry the row's diagonal tile too, as 64-wide slab pairs of its two
+// FP16 parts (hi, lo) at the end of the panel (GemmTask::kdup), both parts meeting the same rows
+// of B, so the whole tile row is one product summed in FP32.  Included by gemm_kernel.h (fragment
+// types, matrix-core wrappers, GemmTask).
 //
 // The general kernel's 128 x 256 blocks move (128 + 256) x 64 operand halves through LDS per
 // 2 x 128 x 256 x 64 products; a 256 x 256 block moves (256 + 256) x 64 for twice the products,
@@ -34,13 +37,14 @@ __device__ __forceinline__ void p16_barrier() {
     __asm__ __volatile__("" ::: "memory");
 }
 
-// Whether the 256 x 256 kernel takes a launch: FP16 operands (A row-major, B column-major), FP64
+// Whether the 256 x 256 kernel can run a task: FP16 operands (A row-major, B column-major), FP64
 // output, no FP16 destination emulation, whole 256 x 256 blocks, whole 64-k slabs, 16-byte
-// aligned rows.
+// aligned rows, diagonal slab pairs (kdup) of whole slabs within K.
 inline bool panel16_fits(const GemmTask& g) {
     return g.ta == DT_F16 && g.tb == DT_F16 && g.tc == DT_F64 && g.transA == 1 && g.transB == 0 && g.kround == 0 &&
            g.M % P16_BM == 0 && g.N % P16_BN == 0 && g.K % P16_BK == 0 && g.K >= P16_BK && g.lda % 8 == 0 &&
-           g.ldb % 8 == 0 && reinterpret_cast<uintptr_t>(g.A) % 16 == 0 && reinterpret_cast<uintptr_t>(g.B) % 16 == 0;
+           g.ldb % 8 == 0 && reinterpret_cast<uintptr_t>(g.A) % 16 == 0 && reinterpret_cast<uintptr_t>(g.B) % 16 == 0 &&
+           g.kdup >= 0 && g.kdup % P16_BK == 0 && 2 * (int64_t)g.kdup <= g.K;
 }
 
 // (a template so that the several sources including this header share one definition)
@@ -73,12 +77,16 @@ void k_panel16(const GemmTask* __restrict__ tasks, int ntasks, int bmc, int bnc,
     }
     if (T.ta != DT_F16 || T.tb != DT_F16 || T.tc != DT_F64 || T.transA != 1 || T.transB != 0 || T.kround != 0 ||
         T.K % P16_BK != 0 || T.K < P16_BK || T.M != bmc * P16_BM || T.N != bnc * P16_BN || T.lda % 8 != 0 ||
-        T.ldb % 8 != 0 || reinterpret_cast<uintptr_t>(T.A) % 16 != 0 || reinterpret_cast<uintptr_t>(T.B) % 16 != 0) {
+        T.ldb % 8 != 0 || reinterpret_cast<uintptr_t>(T.A) % 16 != 0 || reinterpret_cast<uintptr_t>(T.B) % 16 != 0 ||
+        T.kdup < 0 || T.kdup % P16_BK != 0 || 2 * (int64_t)T.kdup > T.K) {
         if (threadIdx.x == 0 && flags) atomicOr(&flags[FLAG_BADTASK], 1ull);
         return;
     }
     const int m0 = (blk % bmc) * P16_BM, n0 = (blk / bmc) * P16_BN;
     const int t = threadIdx.x, l = t % 64, w = t / 64, wm = w % 4, wn = w / 4;
+    // the diagonal tile's (hi, lo) slab pairs start at k = kd.  (Stopping a block after the last
+    // pair that meets its rows, past which the pairs hold zeros, made the launch 1.4% slower.)
+    const int kd = T.K - 2 * T.kdup;
     const int nk = T.K / P16_BK;
 
     // Direct loads of one slab: wave w fills A rows [32 w, 32 w + 32) and B rows [32 w, 32 w + 32),
@@ -89,7 +97,8 @@ void k_panel16(const GemmTask* __restrict__ tasks, int ntasks, int bmc, int bnc,
     const int64_t a_step8 = 8 * T.lda, b_step8 = 8 * T.ldb;   // 8 rows further
     auto issue = [&](int kb) {
         _Float16* st = S + (kb & 1) * P16_STAGE;
-        const int64_t k0 = (int64_t)kb * P16_BK;
+        const int k0 = kb * P16_BK;
+        const int kb0 = k0 >= kd ? kd + (((k0 - kd) >> 1) & ~(P16_BK - 1)) : k0;   // B's k of this slab
 #pragma unroll
         for (int a = 0; a < 4; ++a)
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(a_src + a * a_step8 + k0),
@@ -97,7 +106,7 @@ void k_panel16(const GemmTask* __restrict__ tasks, int ntasks, int bmc, int bnc,
                                              16, 0, 0);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b_src + q * b_step8 + k0),
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(b_src + q * b_step8 + kb0),
                                              (__attribute__((address_space(3))) void*)(st + (P16_BM + 32 * w + 8 * q) * P16_BK),
                                              16, 0, 0);
     };

@@ -27,8 +27,10 @@ __device__ __forceinline__ void philox4x32_10(uint32_t x[4], uint32_t k0, uint32
             k0 += 0x9E3779B9u;
             k1 += 0xBB67AE85u;
         }
-        uint32_t hi0 = __umulhi(0xD2511F53u, x[0]), lo0 = 0xD2511F53u * x[0];
-        uint32_t hi1 = __umulhi(0xCD9E8D57u, x[2]), lo1 = 0xCD9E8D57u * x[2];
+        // each 32 x 32 -> 64-bit product in one multiply-add (both halves at once)
+        const uint64_t p0 = (uint64_t)0xD2511F53u * x[0], p1 = (uint64_t)0xCD9E8D57u * x[2];
+        const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
         uint32_t n0 = hi1 ^ x[1] ^ k0, n2 = hi0 ^ x[3] ^ k1;
         x[0] = n0; x[1] = lo1; x[2] = n2; x[3] = lo0;
     }
@@ -410,36 +412,45 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         g.kround = kround;     // cast16 of the diagonal product (Algorithm 1)
         return g;
     };
-    struct Launch { int64_t b0, b1; int compute; };
+    // p16: a launch of the 256 x 256 row-panel kernel (panel16_launch)
+    struct Launch { int64_t b0, b1; int compute; bool p16; };
     std::vector<Launch> launches;
-    if (fused) {
-        for (int64_t k = 0; k < nt; ++k) tasks.push_back(diag_task(k, 0.0));
-        launches.push_back(Launch{0, nt, amp ? DT_F32 : DT_F64});
-        // off-diagonal part of tile row i: one product of the row panel (nb x i nb) with
-        // B[0 : i nb], longest rows first: FP16 (the row-major cast16 panels) or FP64 (the tiles)
-        std::vector<GemmTask> od;
-        for (int64_t i = nt - 1; i >= 1; --i) {
-            GemmTask g{};
-            if (amp) {
-                g.A = L->l16_panel(i); g.ta = DT_F16; g.lda = i * nb; g.transA = 1;
-            } else {
-                g.A = L->tile(i, 0); g.ta = DT_F64; g.lda = nb; g.transA = 0;
-            }
-            g.B = B; g.tb = amp ? DT_F16 : DT_F64; g.ldb = rows; g.transB = 0;
-            g.C = d_M + i * nb; g.tc = DT_F64; g.ldc = ldm;
-            g.M = (int)nb; g.N = (int)cols; g.K = (int)(i * nb);
-            g.m_store = (int32_t)std::min<int64_t>(nb, n - i * nb); g.n_store = (int32_t)nsim;
-            g.alpha = 1.0; g.beta = 1.0;
-            g.kround = kround;   // GEMM16 stores its destination in FP16 after each k-task
-            od.push_back(g);
+    // Tile row i of the product as one task: the row panel times B[0 : i nb] (off-diagonal tiles),
+    // longest rows first: FP16 (the row-major FP16 panels) or FP64 (the tiles).  With `whole`, the
+    // FP16 panel's two parts of the diagonal tile join it (K = (i + 2) nb, the last nb values of k
+    // reusing B's rows of tile i), so one launch on the 256 x 256 kernel forms the whole row.
+    auto row_task = [&](int64_t i, bool whole) {
+        GemmTask g{};
+        if (amp) {
+            g.A = L->l16_panel(i); g.ta = DT_F16; g.lda = L->l16_ld(i); g.transA = 1;
+        } else {
+            g.A = L->tile(i, 0); g.ta = DT_F64; g.lda = nb; g.transA = 0;
         }
+        g.B = B; g.tb = amp ? DT_F16 : DT_F64; g.ldb = rows; g.transB = 0;
+        g.C = d_M + i * nb; g.tc = DT_F64; g.ldc = ldm;
+        g.M = (int)nb; g.N = (int)cols; g.K = (int)((whole ? i + 2 : i) * nb);
+        g.kdup = whole ? (int32_t)nb : 0;
+        g.m_store = (int32_t)std::min<int64_t>(nb, n - i * nb); g.n_store = (int32_t)nsim;
+        g.alpha = 1.0; g.beta = whole ? 0.0 : 1.0;
+        g.kround = kround;   // GEMM16 stores its destination in FP16 after each k-task
+        return g;
+    };
+    const bool whole_rows = fused && amp && !emu && panel16_takes(row_task(nt - 1, true), (int)nt);
+    if (fused) {
+        if (!whole_rows) {
+            for (int64_t k = 0; k < nt; ++k) tasks.push_back(diag_task(k, 0.0));
+            launches.push_back(Launch{0, nt, amp ? DT_F32 : DT_F64, false});
+        }
+        std::vector<GemmTask> od;
+        for (int64_t i = nt - 1; i >= (whole_rows ? 0 : 1); --i) od.push_back(row_task(i, whole_rows));
         // Task t of a batched launch runs on XCD t mod 8.  Reversing every second group of eight
         // (a snake order) gives each XCD a near-equal share of the K = i nb work; in plain order
         // XCD 0 gets the longest row of every group (15% above the mean at 98 tile rows).
         for (size_t g0 = 8; g0 < od.size(); g0 += 16)
             std::reverse(od.begin() + (std::ptrdiff_t)g0, od.begin() + (std::ptrdiff_t)std::min(g0 + 8, od.size()));
         if (!od.empty()) {
-            launches.push_back(Launch{(int64_t)tasks.size(), (int64_t)(tasks.size() + od.size()), amp ? DT_F16 : DT_F64});
+            launches.push_back(Launch{(int64_t)tasks.size(), (int64_t)(tasks.size() + od.size()), amp ? DT_F16 : DT_F64,
+                                      whole_rows});
             tasks.insert(tasks.end(), od.begin(), od.end());
         }
     } else {
@@ -447,7 +458,7 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         // storage type (one typed kernel per launch)
         for (int64_t k = 0; k < nt; ++k) {
             tasks.push_back(diag_task(k, k == 0 ? 0.0 : 1.0));
-            launches.push_back(Launch{(int64_t)tasks.size() - 1, (int64_t)tasks.size(), amp ? DT_F32 : DT_F64});
+            launches.push_back(Launch{(int64_t)tasks.size() - 1, (int64_t)tasks.size(), amp ? DT_F32 : DT_F64, false});
             for (int ta = DT_F64; ta <= DT_F16; ++ta) {
                 const int64_t b0 = (int64_t)tasks.size();
                 for (int64_t i = k + 1; i < nt; ++i) {
@@ -462,7 +473,7 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
                     g.alpha = 1.0; g.beta = k == 0 ? 0.0 : 1.0;
                     tasks.push_back(g);
                 }
-                if ((int64_t)tasks.size() > b0) launches.push_back(Launch{b0, (int64_t)tasks.size(), amp ? DT_F16 : DT_F64});
+                if ((int64_t)tasks.size() > b0) launches.push_back(Launch{b0, (int64_t)tasks.size(), amp ? DT_F16 : DT_F64, false});
             }
         }
     }
@@ -481,11 +492,16 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     GPEX_HIP(ctx, hipGetLastError());
     if (ctx->timing) (void)hipEventRecord(ev[1], s);
     int r = GPEX_OK;
+    // the row panels' launch (timed on its own): the last one of the fused product
+    const size_t q_rows = fused && launches.size() > (whole_rows ? 0u : 1u) ? launches.size() - 1 : launches.size();
     for (size_t q = 0; q < launches.size() && r >= 0; ++q) {
         const Launch& Lq = launches[q];
-        if (ctx->timing && fused && q == 1) (void)hipEventRecord(ev[4], s);
-        r = gemm_launch(ctx, s, Lq.compute, d_tasks + Lq.b0, (int)(Lq.b1 - Lq.b0), tasks[(size_t)Lq.b0], GEMM_TRMM);
-        if (ctx->timing && fused && q == 1) (void)hipEventRecord(ev[5], s);
+        if (ctx->timing && q == q_rows) (void)hipEventRecord(ev[4], s);
+        if (Lq.p16)
+            r = panel16_launch(ctx, s, d_tasks + Lq.b0, (int)(Lq.b1 - Lq.b0), tasks[(size_t)Lq.b0]);
+        else
+            r = gemm_launch(ctx, s, Lq.compute, d_tasks + Lq.b0, (int)(Lq.b1 - Lq.b0), tasks[(size_t)Lq.b0], GEMM_TRMM);
+        if (ctx->timing && q == q_rows) (void)hipEventRecord(ev[5], s);
     }
     if (ctx->timing) {
         (void)hipEventRecord(ev[2], s);
@@ -505,10 +521,11 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         float a = 0, b = 0, c = 0;
         (void)hipEventElapsedTime(&a, ev[0], ev[3]);
         (void)hipEventElapsedTime(&b, ev[1], ev[2]);
-        if (fused && launches.size() > 1) (void)hipEventElapsedTime(&c, ev[4], ev[5]);
+        if (q_rows < launches.size()) (void)hipEventElapsedTime(&c, ev[4], ev[5]);
         ctx->timings[10] = a;
         ctx->timings[11] = b;
         ctx->timings[18] = c;
+        ctx->timings[19] = whole_rows ? 1.0 : 0.0;
         for (auto& e2 : ev) (void)hipEventDestroy(e2);
     }
     if (diag) {

@@ -198,10 +198,12 @@ int gpex_tiled_block(gpex_ctx_t ctx, gpex_tiled_t t, int64_t r0, int64_t c0, int
  * tiles (before the factorisation s^2 V in reduced-precision tiles and V in FP64 tiles; L_s after
  * it; entries above the diagonal tiles read 0),
  * which = 1 the FP16 copy of the off-diagonal factor tiles that the simulation product multiplies
- * with (Algorithm 1, cast16 of L_s; entries in diagonal tiles and above read 0; needs a factor
- * computed with amp = 1, else GPEX_ERR_STATE).  Lets a caller check that every stored value is a
- * value of its tile's precision and that the FP16 copy is cast16 of the stored factor.  Block
- * bounds and ld as in gpex_tiled_block.  Enqueued on ctx. */
+ * with (Algorithm 1, cast16 of L_s; entries in diagonal tiles and above read 0), which = 2 the
+ * diagonal tiles as the simulation product's two FP16 parts hi + lo (hi = cast16(L_s), lo =
+ * cast16(L_s - hi); entries outside diagonal tiles read 0); which = 1 and 2 need a factor of more
+ * than one tile row computed with amp = 1, else GPEX_ERR_STATE.  Lets a caller check that every
+ * stored value is a value of its tile's precision and that the FP16 copy is cast16 of the stored
+ * factor.  Block bounds and ld as in gpex_tiled_block.  Enqueued on ctx. */
 int gpex_tiled_block_raw(gpex_ctx_t ctx, gpex_tiled_t t, int which, int64_t r0, int64_t c0, int64_t rows,
                          int64_t cols, double* d_out, int64_t ld);
 int gpex_tiled_destroy(gpex_tiled_t t);
@@ -215,8 +217,10 @@ int gpex_tiled_destroy(gpex_tiled_t t);
  * converted to it (FP16 tiles on FP16 matrix cores with FP32 accumulation and one FP16 rounding per
  * update), diagonal tiles in FP64.  With amp = 1 the panel solves also write the FP16 copy of
  * each off-diagonal factor tile that gpex_trmm_sim multiplies with (Algorithm 1, cast16; the
- * FP16 updates read their operands from it too), and FP32 / FP64 copies of the panel tiles that
- * feed updates of another precision (workspace: up to 24 nb^2 (NT - 1) bytes).
+ * FP16 updates read their operands from it too), once the factor is complete each diagonal tile
+ * as two FP16 parts beside it (hi = cast16(L_kk), lo = cast16(L_kk - hi)), and FP32 / FP64
+ * copies of the panel tiles that feed updates of another precision (workspace: up to
+ * 24 nb^2 (NT - 1) bytes).
  * *info = 0, or the 1-based column of the first non-positive pivot: then GPEX_ERR_NOT_SPD and the
  * handle is marked failed (its tiles were overwritten in place): gpex_potrf_mp, gpex_trmm_sim,
  * gpex_tiled_block and gpex_tiled_to_dense then return GPEX_ERR_STATE.  GPEX_WARN_FP16_OVERFLOW
@@ -236,10 +240,12 @@ int gpex_normals(gpex_ctx_t ctx, uint64_t seed, uint32_t stream, int64_t n, int6
 /* M = L_s B with B = Z / s (Algorithm 1 and Eq. 3 of the mixed-precision page).  Z is either
  * the explicit d_Z (n x nsim, leading dimension n) or, when d_Z is NULL, the seeded normals of
  * gpex_normals(seed, stream 0).  With amp = 1, B is rounded to FP16, each off-diagonal L tile
- * is converted to FP16 and multiplied on FP16 matrix cores, the diagonal tile is applied in
- * FP32, all with FP32 accumulation, and M is written in FP64 (with fp16_dest_emulation the
- * running sum is kept in FP16 between k-tasks, see gpex_prec_opts); with amp = 0 everything is
- * FP64.  d_M: n x nsim, leading dimension ldm >= n; exactly rows [0, n) and columns [0, nsim)
+ * is converted to FP16 and multiplied on FP16 matrix cores, the diagonal tile is applied at
+ * about FP32 accuracy (where the 256 x 256 row-panel kernel takes the product: its two FP16
+ * parts hi + lo on FP16 matrix cores, summed with the row; otherwise an FP32 copy on FP32
+ * matrix cores), all with FP32 accumulation, and M is written in FP64 (with
+ * fp16_dest_emulation the running sum is kept in FP16 between k-tasks, see gpex_prec_opts);
+ * with amp = 0 everything is FP64.  d_M: n x nsim, leading dimension ldm >= n; exactly rows [0, n) and columns [0, nsim)
  * are written (the products compute the tile padding but do not store it).  diag (may be NULL)
  * receives the plan's diagnostics with norm_B.  Requires a factored matrix (GPEX_ERR_STATE
  * otherwise).  Returns GPEX_WARN_FP16_OVERFLOW (M is written) when an entry of Z / s overflowed
@@ -328,8 +334,10 @@ int gpex_excursion_regions_noalloc(gpex_ctx_t ctx, const double* d_M, int64_t ld
  *          (the last tile row and column hold n - (NT - 1) nb rows);
  *   [15..17] busy ms of the trailing-update launches per precision: the union of their launch
  *          intervals (launches of the two streams overlap, so [1], [4], [7] may exceed it);
- *   [18] trmm: ms of the off-diagonal (row-panel) launch of the simulation product;
- *   [19..31] reserved (0). */
+ *   [18] trmm: ms of the row-panel launch of the simulation product (off-diagonal tiles, with
+ *          the diagonal tiles where the 256 x 256 kernel takes them);
+ *   [19] trmm: 1 when that launch applied the diagonal tiles too, else 0;
+ *   [20..31] reserved (0). */
 int gpex_ctx_set_timing(gpex_ctx_t ctx, int on);
 int gpex_ctx_timings(gpex_ctx_t ctx, double* out32);
 

@@ -532,7 +532,8 @@ def test_trmm_256_blocks_rows_and_store_guard(ctx):
     rows of M, including rows of every 64-row wave group and of the ragged last tile row, equal
     the factor's row times the oracle's seeded normals (to FP16 accuracy), a call through a
     larger leading dimension stores exactly rows [0, n) and columns [0, nsim), bitwise as with
-    ldm = n, and the general kernel gives the same columns bitwise."""
+    ldm = n, and the general kernel (diagonal tiles in FP32 in a launch of their own) gives the same
+    columns to FP32 rounding."""
     import ctypes
     n, nb, nsim, seed, extra_rows = 33500, 512, 2000, 2013, 37
     x, y, params = setup_case(n, nb, 1.5, 0.1, 13)
@@ -559,11 +560,46 @@ def test_trmm_256_blocks_rows_and_store_guard(ctx):
     assert np.array_equal(got[:nsim, :n], M_ref.T.cpu().numpy())
     assert np.all(got[:nsim, n:] == sentinel)
     assert np.all(got[nsim, :] == sentinel)
-    # 1,920 columns (not a multiple of 256) take the general 128 x 256 kernel; column j of the
-    # seeded normals does not depend on nsim and both kernels sum each output's k in the same
-    # order, so the shared columns agree bitwise
+    # 1,920 columns (not a multiple of 256) take the general 128 x 256 kernel for the off-diagonal
+    # tiles and an FP32 launch for the diagonal ones; column j of the seeded normals does not depend
+    # on nsim, so the shared columns differ only by the diagonal's FP16 parts (about 2^-22 of each
+    # entry) and FP32 rounding of the sums
     M_gen, _ = g.trmm_sim(ctx, A, 1920, seed=seed)
-    assert np.array_equal(M_gen.cpu().numpy(), M_ref[:, :1920].cpu().numpy())
+    Mg, Mp = M_gen.cpu().numpy(), M_ref[:, :1920].cpu().numpy()
+    assert np.linalg.norm(Mg - Mp) / np.linalg.norm(Mp) <= 1e-5
+    A.close()
+
+
+def test_trmm_diagonal_fp16_parts(ctx):
+    """The two FP16 parts of each diagonal tile that the row-panel kernel multiplies with:
+    hi = cast16(L_kk) and lo = cast16(L_kk - hi) of the stored factor, exactly (numpy's
+    float64 -> float16 conversion rounds to nearest even), zeros above the diagonal and outside
+    the diagonal tiles; and rows of tile rows 0 and 1 of the product (16 row panels x 4 x 16
+    blocks of 256 x 256, so the diagonal tiles join the row panels' launch) equal the factor's rows
+    times the seeded normals to FP16 accuracy."""
+    n, nb, nsim, seed = 16000, 1024, 4096, 2021
+    x, y, params = setup_case(n, nb, 1.5, 0.1, 17)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=1e-8)
+    assert g.potrf_mp(ctx, A) == 0
+    nt = (n + nb - 1) // nb
+    for k in range(nt):
+        r0, m = k * nb, min(nb, n - k * nb)
+        t = np.tril(A.block_raw(r0, r0, m, m).cpu().numpy())
+        P = A.block_raw(r0, 0, m, r0 + m, diag_parts=True).cpu().numpy()
+        hi = t.astype(np.float16)
+        lo = (t - hi.astype(np.float64)).astype(np.float16)
+        assert np.array_equal(P[:, r0:], hi.astype(np.float64) + lo.astype(np.float64)), k
+        assert np.all(np.abs(P[:, r0:] - t) <= 2.0 ** -22 * np.abs(t) + 2.0 ** -25), k
+        assert not np.any(P[:, :r0]), k
+    M, _ = g.trmm_sim(ctx, A, nsim, seed=seed)
+    rows = [0, 1, 255, 256, 777, 1023, 1024, 1500, 2047]
+    Z = oracle.normals(seed, 0, n, nsim, rows=(0, max(rows) + 1))
+    Mr = M[rows].cpu().numpy()
+    for k, r in enumerate(rows):
+        lr = A.block(r, 0, 1, r + 1).cpu().numpy()[0]
+        ref = lr @ Z[:r + 1]
+        er = np.linalg.norm(Mr[k] - ref) / np.linalg.norm(ref)
+        assert er <= 1e-2, (r, er)
     A.close()
 
 
