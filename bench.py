@@ -282,6 +282,10 @@ def study(args):
     f64 = lambda a: torch.tensor(np.ascontiguousarray(a), dtype=torch.float64, device=dev)   # noqa: E731
     reps, nsim, nb, u, level, tau2 = args.study_reps, args.study_nsim, 512, 10.0, 0.9, 0.01
     ranges = [rg for rg in STUDY_RANGES if rg[0] in args.study_ranges.split(",")]
+    want = args.study_levels.split(",") if args.study_levels != "all" else [lv[0] for lv in STUDY_LEVELS]
+    levels = [lv for lv in STUDY_LEVELS if lv[0] in want]
+    if not levels or levels[0][0] != "DP":
+        raise SystemExit("--study-levels must include DP (the reference of the cell differences)")
     xp, yp = syn.grid_centres(120)
     xo, yo = syn.uniform_locations(3200, 3005)
     xp, yp, _ = syn.ordered_locations(xp, yp)
@@ -294,7 +298,8 @@ def study(args):
     loc, loc_o, loc_p = f64(np.r_[x, y]), f64(np.r_[xo, yo]), f64(np.r_[xp, yp])
     ctx = g.Context(0)
     out = {"design": {"n_p": n_p, "n_o": n_o, "nsim": nsim, "reps": reps, "u": u, "level": level, "tau2": tau2,
-                      "nb": nb, "trend": [0.0, 15.0, 10.0], "nu": 0.5}, "ranges": []}
+                      "nb": nb, "trend": [0.0, 15.0, 10.0], "nu": 0.5, "levels": [lv[0] for lv in levels]},
+           "ranges": []}
     t_start = time.time()
     M = g.colmajor(n, nsim, ctx)
     for name, beta in ranges:
@@ -313,7 +318,7 @@ def study(args):
         T = T + mean[:, None]
         AV.close()
         facs, rows, seen = {}, [], {}
-        for label, amp, tol, emu in STUDY_LEVELS:
+        for label, amp, tol, emu in levels:
             A = g.cov_gen(ctx, loc, n, params, nb, amp=amp, tol=tol, diag_add=diag_add, fp16_dest=emu)
             rec = {"level": label, "tiles_fp64_fp32_fp16": A.diag["tiles"], "s": A.diag["s"],
                    "eq10_pass": A.diag["eq10_pass"], "eq11_pass": A.diag["eq11_pass"],
@@ -403,6 +408,8 @@ def main():
     ap.add_argument("--study-reps", type=int, default=200)
     ap.add_argument("--study-nsim", type=int, default=80000)
     ap.add_argument("--study-ranges", default="weak,medium,strong")
+    ap.add_argument("--study-levels", default="all",
+                    help="comma-separated level labels (DP, 1e-4 ... 1e-14, '1e-4 fp16-dest'), or all")
     ap.add_argument("--sweep-nsim", type=int, default=2048)
     ap.add_argument("--sweep-max-n", type=int, default=131072)
     ap.add_argument("--sweep-n", default="", help="comma-separated sizes instead of the sweep's list (multiples of 1024)")

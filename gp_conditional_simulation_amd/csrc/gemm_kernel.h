@@ -342,8 +342,10 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
                     }
         }
     }
-    // round the accumulator to FP16 (the destination store of one k-task)
-    auto round16 = [&]() {
+    // round the accumulator to FP16 (the destination store of one k-task).  The lambdas that touch
+    // the accumulator are forced inline: when the FP16-destination variant grew past the inliner's
+    // threshold, the accumulators went to scratch memory and that kernel ran 16x slower.
+    auto round16 = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -351,7 +353,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[i][j][r] = (float)(_Float16)acc[i][j][r];
     };
-    auto task_end = [&](int kb) {
+    auto task_end = [&](int kb) __attribute__((always_inline)) {
         if constexpr (EMU) {
             if (((kb + 1) * BK) % T.kround == 0) round16();
         }
@@ -387,7 +389,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     constexpr bool IL = INTERLEAVE != 0;
     typedef typename FragT<CT>::type FT;
     FT fa[2][4], fb[2][FJ];
-    auto rd = [&](const CT* as, const CT* bs, int st, FT* af, FT* bf) {
+    auto rd = [&](const CT* as, const CT* bs, int st, FT* af, FT* bf) __attribute__((always_inline)) {
         if constexpr (sizeof(CT) == 2) {
             const int ks = st * 32;
 #pragma unroll
@@ -412,7 +414,7 @@ void k_gemm_t(const GemmTask* __restrict__ tasks, GemmTask one, int ntasks, int 
     // order per step: next fragments' LDS reads, this step's share of the register vectors
     // (store, reload), the products; in the last step the barrier and the next slab's first reads
     // come ahead of the deferred products.
-    auto slab = [&](int kb, auto wr_t, auto ld_t) {
+    auto slab = [&](int kb, auto wr_t, auto ld_t) __attribute__((always_inline)) {
         constexpr bool WR = decltype(wr_t)::value;
         constexpr bool LD = decltype(ld_t)::value;
         const int cur = kb & 1;
