@@ -275,12 +275,16 @@ def potrf_mp_emul(A, nb: int, pmap) -> tuple[np.ndarray, int]:
     return A, int(info)
 
 
-def trmm_mp_emul(Ls, nb: int, s: float, Z, fp16_dest: bool = False) -> np.ndarray:
+def trmm_mp_emul(Ls, nb: int, s: float, Z, fp16_dest: bool = False, diag16: bool = False) -> np.ndarray:
     """Emulated mixed-precision TRMM of Algorithm 1: M = L_s round16(Z / s) with FP32 diagonal
     products, FP16 off-diagonal products and FP32 sums; fp16_dest keeps the destination in FP16
-    between k-tasks as the printed algorithm does."""
+    between k-tasks as the printed algorithm does; diag16 takes each diagonal tile as two FP16
+    parts (hi, lo) inside one FP32 sum with the row's off-diagonal products."""
+    if fp16_dest and diag16:
+        raise ValueError("fp16_dest and diag16 are separate modes")
     Ls, Z = _f(Ls), _f(Z)
     n, nsim = Z.shape
     M = np.empty((n, nsim), order="F")
-    lib().orc_trmm_mp_emul(Ls, Ls.shape[0], n, nb, float(s), Z, n, nsim, int(bool(fp16_dest)), M, n)
+    mode = 2 if diag16 else int(bool(fp16_dest))
+    lib().orc_trmm_mp_emul(Ls, Ls.shape[0], n, nb, float(s), Z, n, nsim, mode, M, n)
     return M

@@ -511,7 +511,11 @@ int64_t orc_potrf_mp_emul(double* A, int64_t n, int64_t lda, int64_t nb, const u
  * fp16_dest = 1 (Algorithm 1 as printed, FP16 destination storage): the diagonal product is
  * rounded to FP16, then for k = 0 .. i-1 the running value enters an FP32 sum with tile k's
  * products and the result is rounded to FP16.  fp16_dest = 0: one FP32 sum of all off-diagonal
- * products of the row, added in FP64 to the FP32 diagonal product.  M is FP64. */
+ * products of the row, added in FP64 to the FP32 diagonal product.  fp16_dest = 2 (the whole-row
+ * form, a reading of ours: the pages fix no format for the diagonal product): the diagonal tile
+ * enters as two FP16 parts, hi = cast16(L) and lo = cast16(L - hi), both multiplied with B_i, and
+ * the row's off-diagonal and diagonal products form one FP32 sum (off-diagonal columns first, then
+ * hi and lo of each diagonal column in turn).  M is FP64. */
 void orc_trmm_mp_emul(const double* Ls, int64_t ldl, int64_t n, int64_t nb, double s, const double* Z,
                       int64_t ldz, int64_t nsim, int fp16_dest, double* M, int64_t ldm) {
     int64_t nt = (n + nb - 1) / nb;
@@ -522,6 +526,18 @@ void orc_trmm_mp_emul(const double* Ls, int64_t ldl, int64_t n, int64_t nb, doub
         for (int64_t ti = 0; ti < nt; ++ti) {
             int64_t r0 = ti * nb, r1 = (ti + 1) * nb < n ? (ti + 1) * nb : n;
             for (int64_t r = r0; r < r1; ++r) {
+                if (fp16_dest == 2) {
+                    float acc = 0.0f;
+                    for (int64_t m = 0; m < r0; ++m) acc += (float)orc_round_fp16(Ls[IDX(r, m, ldl)]) * (float)b[m];
+                    for (int64_t m = r0; m <= r; ++m) {
+                        const double hi = orc_round_fp16(Ls[IDX(r, m, ldl)]);
+                        const double lo = orc_round_fp16(Ls[IDX(r, m, ldl)] - hi);
+                        acc += (float)hi * (float)b[m];
+                        acc += (float)lo * (float)b[m];
+                    }
+                    M[IDX(r, j, ldm)] = (double)acc;
+                    continue;
+                }
                 float d = 0.0f;
                 for (int64_t m = r0; m <= r; ++m) d += (float)Ls[IDX(r, m, ldl)] * (float)b[m];
                 if (fp16_dest) {

@@ -603,6 +603,34 @@ def test_trmm_diagonal_fp16_parts(ctx):
     A.close()
 
 
+def test_trmm_whole_rows_against_emulation(ctx):
+    """The whole-row launch (each diagonal tile as two FP16 parts inside its row's FP32 sum) against
+    the oracle's emulation of that form: the leading 4 tile rows and 16 columns of an explicit-Z
+    product large enough for the 256 x 256 row-panel kernel (16 row panels x 4 x 16 blocks).  Rows
+    below 4 nb depend only on the leading block of the factor, so the emulation runs on that block;
+    the two sides differ only in FP32 summation order."""
+    n, nb, nsim, m, cols = 16000, 1024, 4096, 4096, 16
+    x, y, params = setup_case(n, nb, 1.5, 0.1, 19)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=1e-8)
+    assert g.potrf_mp(ctx, A) == 0
+    s = A.diag["s"]
+    Z = syn.explicit_normals(n, nsim, 2031)
+    ctx.set_timing(True)
+    try:
+        M, _ = g.trmm_sim(ctx, A, nsim, Z=dev_cm(Z))
+        assert ctx.timings()["trmm_rows_with_diagonal"], "the row-panel kernel did not take the diagonal tiles"
+    finally:
+        ctx.set_timing(False)
+    Ls = np.tril(A.block_raw(0, 0, m, m).cpu().numpy())
+    Mg = M[:m, :cols].cpu().numpy()
+    Me2 = oracle.trmm_mp_emul(Ls, nb, s, Z[:m, :cols], diag16=True)
+    Me0 = oracle.trmm_mp_emul(Ls, nb, s, Z[:m, :cols])
+    e2, e0 = rel(Mg, Me2), rel(Mg, Me0)
+    print(f"map {A.diag['tiles']}: whole-row launch vs emulation {e2:.2e} (vs the FP32-diagonal emulation {e0:.2e})")
+    assert e2 <= 1e-5
+    A.close()
+
+
 def test_single_tile_mixed_precision_simulation(ctx):
     """One tile (no off-diagonal work): the mixed-precision product is the FP32 diagonal alone,
     applied to B = Z / s rounded to FP16, with the scale s of Eq. 12 (no reduced-precision tile:

@@ -109,6 +109,44 @@ def test_emulated_trmm_exact_on_integers(fp16_dest):
     assert np.array_equal(M, L @ B)
 
 
+def test_emulated_trmm_diagonal_parts_exact():
+    """Whole-row form: diagonal entries 1 + 2^-12 k (hi = 1 in binary16, lo = 2^-12 k exactly) and
+    small integer off-diagonal entries and B: every part, product and partial sum is exact in
+    binary32, so the result is exactly L B; dropping lo, or pairing it with another row of B,
+    changes it."""
+    n, nb, nsim, s = 192, 64, 5, 4.0
+    rng = np.random.default_rng(7)
+    L = np.tril(rng.integers(-3, 4, (n, n)).astype(np.float64), -1)
+    for i in range(0, n, nb):   # diagonal tiles: 1 + 2^-12 k, k in [-3, 3], on and below the diagonal
+        blk = np.tril(1.0 + rng.integers(-3, 4, (min(nb, n - i),) * 2) * 2.0 ** -12)
+        L[i:i + nb, i:i + nb] = blk
+    B = rng.integers(-4, 5, (n, nsim)).astype(np.float64)
+    M = oracle.trmm_mp_emul(L, nb, s, s * B, diag16=True)
+    assert np.array_equal(M, L @ B)
+    # the parts really split: hi alone (lo dropped) misses the 2^-12 terms
+    hi_only = np.where(np.arange(n)[:, None] // nb == np.arange(n)[None, :] // nb, np.round(L), L)
+    assert not np.array_equal(M, hi_only @ B)
+    # the FP32-diagonal form agrees here too (cast32 of 1 + 2^-12 k is exact)
+    assert np.array_equal(oracle.trmm_mp_emul(L, nb, s, s * B), M)
+
+
+def test_emulated_trmm_diagonal_parts_accuracy():
+    """On a real factor the whole-row form stays within the FP16 rounding of B of the exact product,
+    and within about 2^-22 of the FP32-diagonal form (the parts carry L to about 22 bits)."""
+    n, nb, nsim, s = 640, 64, 16, 300.0
+    V, _ = _case(n, nb, 1.5, 0.1, 4, 0.0, True)
+    L, _ = oracle.potrf(V)
+    Ls = s * L
+    Z = syn.explicit_normals(n, nsim, 9)
+    M0 = oracle.trmm_mp_emul(Ls, nb, s, Z)
+    M2 = oracle.trmm_mp_emul(Ls, nb, s, Z, diag16=True)
+    scale = np.abs(Ls) @ np.abs(Z / s)
+    assert np.all(np.abs(M2 - L @ Z) <= 3 * 2.0 ** -11 * scale + 1e-12)
+    assert np.all(np.abs(M2 - M0) <= 2.0 ** -20 * scale + 1e-12)
+    with pytest.raises(ValueError):
+        oracle.trmm_mp_emul(Ls, nb, s, Z, fp16_dest=True, diag16=True)
+
+
 def test_emulated_trmm_fp16_destination_rounding():
     n, nb, nsim, s = 640, 64, 16, 300.0
     V, _ = _case(n, nb, 1.5, 0.1, 4, 0.0, True)
