@@ -415,10 +415,11 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     // p16: a launch of the 256 x 256 row-panel kernel (panel16_launch)
     struct Launch { int64_t b0, b1; int compute; bool p16; };
     std::vector<Launch> launches;
-    // Tile row i of the product as one task: the row panel times B[0 : i nb] (off-diagonal tiles),
-    // longest rows first: FP16 (the row-major FP16 panels) or FP64 (the tiles).  With `whole`, the
-    // FP16 panel's two parts of the diagonal tile join it (K = (i + 2) nb, the last nb values of k
-    // reusing B's rows of tile i), so one launch on the 256 x 256 kernel forms the whole row.
+    // Tile row i of the product as one task: the row panel times B[0 : i nb] (off-diagonal tiles):
+    // FP16 (the row-major FP16 panels) or FP64 (the tiles).  With `whole`, the FP16 panel's two
+    // parts of the diagonal tile join it (K = (i + 2) nb: the last 2 nb values of k are the tile's
+    // (hi, lo) slab pairs, both meeting B's rows of tile i), so one launch on the 256 x 256 kernel
+    // forms the whole row and stores it once (beta = 0).
     auto row_task = [&](int64_t i, bool whole) {
         GemmTask g{};
         if (amp) {
@@ -441,7 +442,7 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
             for (int64_t k = 0; k < nt; ++k) tasks.push_back(diag_task(k, 0.0));
             launches.push_back(Launch{0, nt, amp ? DT_F32 : DT_F64, false});
         }
-        std::vector<GemmTask> od;
+        std::vector<GemmTask> od;   // longest rows first
         for (int64_t i = nt - 1; i >= (whole_rows ? 0 : 1); --i) od.push_back(row_task(i, whole_rows));
         // Task t of a batched launch runs on XCD t mod 8.  Reversing every second group of eight
         // (a snake order) gives each XCD a near-equal share of the K = i nb work; in plain order

@@ -603,6 +603,28 @@ def test_trmm_diagonal_fp16_parts(ctx):
     A.close()
 
 
+@pytest.mark.parametrize("nb", [160, 320])
+def test_diagonal_fp16_parts_small_tiles(ctx, nb):
+    """The diagonal tiles' FP16 parts for tile orders that are not a multiple of 256: 160 (not a
+    multiple of 64: one (hi, lo) pair as wide as the tile) and 320 (five pairs of 64), with a ragged
+    last tile; hi + lo is exactly binary16(L) + binary16(L - binary16(L)) of the stored factor."""
+    n = 1000
+    x, y, params = setup_case(n, nb, 1.5, 0.05, 23)
+    A = g.cov_gen(ctx, dev(np.r_[x, y]), n, params, nb, amp=1, tol=1e-6)
+    assert g.potrf_mp(ctx, A) == 0
+    L = np.tril(A.block_raw(0, 0, n, n).cpu().numpy())
+    P = A.block_raw(0, 0, n, n, diag_parts=True).cpu().numpy()
+    for k in range((n + nb - 1) // nb):
+        sl = slice(k * nb, min((k + 1) * nb, n))
+        t = L[sl, sl]
+        hi = t.astype(np.float16)
+        lo = (t - hi.astype(np.float64)).astype(np.float16)
+        assert np.array_equal(P[sl, sl], hi.astype(np.float64) + lo.astype(np.float64)), k
+        P[sl, sl] = 0.0
+    assert not np.any(P)
+    A.close()
+
+
 def test_trmm_whole_rows_against_emulation(ctx):
     """The whole-row launch (each diagonal tile as two FP16 parts inside its row's FP32 sum) against
     the oracle's emulation of that form: the leading 4 tile rows and 16 columns of an explicit-Z
