@@ -183,7 +183,10 @@ def krige_bench(args):
     (20,000 prediction + 20,000 observation locations, Matern nu = 3/2, range 0.1, trend
     (0.5, 1, -1), tau^2 = 0.01, FP64, 1,000 simulations, u = 1, level 0.9).  The observations are
     the trend plus seeded N(0, 1) noise: the work does not depend on their values.  Reported as
-    nsim / (T_trmm + T_cond+scan) with the factor amortised, and per phase."""
+    nsim / (T_trmm + T_cond+scan) with the factor amortised, and per phase.  The same step with the
+    joint factor in mixed precision (tolerance 1e-8, FP16 simulation product; the kriging stays
+    FP64) is reported beside it, with the share of cells whose region membership differs from the
+    FP64 step's."""
     import numpy as np
     import torch
 
@@ -206,12 +209,13 @@ def krige_bench(args):
     M = g.colmajor(w.n, w.nsim, ctx)
     torch.cuda.synchronize()
 
-    def step():
+    def step(amp=w.amp, tol=w.tol, dadd=diag_add):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         ev[0].record()
         W, zhat, v, info = g.krige(ctx, loc_o, n_o, loc_p, n_p, dy, 3, params, w.tau2, w.nb)
         ev[1].record()
-        A = g.cov_gen(ctx, loc, w.n, dict(params, nugget=0.0), w.nb, amp=w.amp, tol=w.tol, diag_add=diag_add)
+        A = g.cov_gen(ctx, loc, w.n, dict(params, nugget=0.0), w.nb, amp=amp, tol=tol, diag_add=dadd)
+        tiles = A.diag["tiles"]
         ev[2].record()
         fi = g.potrf_mp(ctx, A)
         ev[3].record()
@@ -225,16 +229,31 @@ def krige_bench(args):
             raise RuntimeError(f"kriging workload failed: krige {info}, potrf {fi}, regions {out['status']}")
         ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
         return dict(zip(("krige", "cov_gen", "potrf", "trmm", "cond_scan_regions"), ms),
-                    cin=int(out["cin"].sum().item()), cout=int(out["cout"].sum().item()))
+                    cin=int(out["cin"].sum().item()), cout=int(out["cout"].sum().item()), tiles=tiles,
+                    cin_mask=out["cin"].clone(), cout_mask=out["cout"].clone())
 
+    keys = ("krige", "cov_gen", "potrf", "trmm", "cond_scan_regions")
+    # The mixed-precision joint factor of the latent block (no nugget) can lose definiteness: then
+    # the mixed-precision steps add 1e-4 sigma^2 on the prediction rows (a documented fallback)
+    A = g.cov_gen(ctx, loc, w.n, dict(params, nugget=0.0), w.nb, amp=1, tol=1e-8, diag_add=diag_add)
+    mp_info = g.potrf_mp(ctx, A)
+    A.close()
+    jitter = 0.0 if mp_info == 0 else 1e-4 * w.sigma2
+    diag_mp = f64(np.r_[np.full(n_p, jitter), np.full(n_o, w.tau2)])
     for i in range(args.warmup):
-        log("warmup", i, step())
-    recs = []
+        log("warmup", i, {k: round(v, 2) for k, v in step().items() if k in keys})
+    recs, recs_mp = [], []
     for i in range(args.steps):
         r = step()
         recs.append(r)
-        log("step", i, {k: round(v, 2) for k, v in r.items()})
-    med = {k: statistics.median(r[k] for r in recs) for k in ("krige", "cov_gen", "potrf", "trmm", "cond_scan_regions")}
+        log("step", i, {k: round(v, 2) for k, v in r.items() if k in keys})
+        r2 = step(amp=1, tol=1e-8, dadd=diag_mp)
+        recs_mp.append(r2)
+        log("step mixed", i, {k: round(v, 2) for k, v in r2.items() if k in keys}, r2["tiles"])
+    med = {k: statistics.median(r[k] for r in recs) for k in keys}
+    med_mp = {k: statistics.median(r[k] for r in recs_mp) for k in keys}
+    d_in = float((recs_mp[-1]["cin_mask"] != recs[-1]["cin_mask"]).double().mean())
+    d_out = float((recs_mp[-1]["cout_mask"] != recs[-1]["cout_mask"]).double().mean())
     cond_flops = 2.0 * n_p * w.nsim * n_o
     krige_flops = n_o ** 3 / 3.0 + 2.0 * n_o ** 2 * n_p
     print(json.dumps({
@@ -247,6 +266,17 @@ def krige_bench(args):
         "joint_potrf_fp64_tflops": round(w.n ** 3 / 3.0 / (med["potrf"] * 1e-3) / 1e12, 1),
         "conditioning_fp64_tflops_lower_bound": round(cond_flops / (med["cond_scan_regions"] * 1e-3) / 1e12, 1),
         "regions_cells": {"cin": recs[-1]["cin"], "cout": recs[-1]["cout"]},
+        "mixed_precision": {
+            "joint_factor": "tolerance 1e-8 (tile-count-scaled rule), FP16 simulation product; kriging FP64",
+            "prediction_row_jitter": jitter,
+            "jitter_reason": (f"without it the mixed-precision factor stops at column {mp_info} (non-positive pivot)"
+                              if mp_info else "none needed"),
+            "tiles_fp64_fp32_fp16": recs_mp[-1]["tiles"],
+            "value": round(w.nsim / ((med_mp["trmm"] + med_mp["cond_scan_regions"]) * 1e-3), 1),
+            "unit": "simulations/s", "phase_ms_median": {k: round(v, 2) for k, v in med_mp.items()},
+            "joint_potrf_fp64_equiv_tflops": round(w.n ** 3 / 3.0 / (med_mp["potrf"] * 1e-3) / 1e12, 1),
+            "regions_cells": {"cin": recs_mp[-1]["cin"], "cout": recs_mp[-1]["cout"]},
+            "cells_differing_from_fp64": {"inner": d_in, "outer": d_out}},
     }), flush=True)
 
 

@@ -297,3 +297,45 @@ def test_kriging_workload_fullsize(ctx):
     log(f"  regions: n_psi {out['n_psi']} n_phi {out['n_phi']} q_out {out['q_out']:.4f} q_in {out['q_in']:.4f} "
         f"|C_out| {int(cout.sum())} |C_in| {int(cin.sum())}")
     A.close()
+    del S, ge, le
+    # the same conditional path with the joint factor in mixed precision (tolerance 1e-8: FP64 and
+    # FP32 tiles) and the FP16 simulation product, same seeds: the simulations agree with the FP64
+    # ones to the FP16 rounding of the product, their mean still matches zhat, and the regions
+    # differ from the FP64 regions in few cells
+    A2 = g.cov_gen(ctx, dev(np.r_[x, y]), n, dict(params, nugget=0.0), w.nb, amp=1, tol=1e-8,
+                   diag_add=dev(diag_add))
+    tiles = A2.diag["tiles"]
+    assert tiles[1] + tiles[2] > 0, tiles
+    info3 = g.potrf_mp(ctx, A2)
+    Mref = M
+    if info3 != 0:
+        # documented fallback: the FP32 tiles' rounding outweighs the smallest eigenvalues of the
+        # latent block (no nugget), so the mixed-precision factor loses definiteness; rerun with
+        # 1e-4 sigma^2 on the prediction rows, and take the FP64 reference of that same matrix
+        log(f"  mixed-precision joint factor: non-positive pivot at column {info3}; 1e-4 sigma^2 on prediction rows")
+        assert 0 < info3 <= n
+        A2.close()
+        diag_j = diag_add.copy()
+        diag_j[:n_p] += 1e-4 * w.sigma2
+        A2 = g.cov_gen(ctx, dev(np.r_[x, y]), n, dict(params, nugget=0.0), w.nb, amp=1, tol=1e-8,
+                       diag_add=dev(diag_j))
+        tiles = A2.diag["tiles"]
+        assert tiles[1] + tiles[2] > 0, tiles
+        assert g.potrf_mp(ctx, A2) == 0
+        Aj = g.cov_gen(ctx, dev(np.r_[x, y]), n, dict(params, nugget=0.0), w.nb, amp=0, diag_add=dev(diag_j))
+        assert g.potrf_mp(ctx, Aj) == 0
+        Mref, _ = g.trmm_sim(ctx, Aj, w.nsim, seed=w.seed_sim)
+        Aj.close()
+    M2, _ = g.trmm_sim(ctx, A2, w.nsim, seed=w.seed_sim)
+    em = float(torch.linalg.norm(M2 - Mref) / torch.linalg.norm(Mref))
+    assert em <= 1e-2, em
+    out2 = g.excursion_regions(ctx, M2, n_p, n_o, w.nsim, w.u, w.level, W=W, y_o=dev(y_obs), zhat=zhat, v=v,
+                               want_S=True)
+    assert out2["status"] == 0
+    zmean2 = (out2["S"].mean(1) - zhat).abs() / se
+    assert float(zmean2.max()) < 6.0
+    d_in = float((out2["cin"] != out["cin"]).double().mean())
+    d_out = float((out2["cout"] != out["cout"]).double().mean())
+    log(f"  mixed precision: tiles {tiles}, M vs FP64 {em:.2e}, cells differing inner {d_in:.2e} outer {d_out:.2e}")
+    assert d_in <= 1e-2 and d_out <= 1e-2
+    A2.close()
