@@ -212,7 +212,7 @@ int gemm1(gpex_ctx_t ctx, int compute, const void* A, int ta, int transA, int64_
           int N, int K, double alpha, double beta);
 
 // Whether the 256 x 256 FP16 row-panel kernel takes a launch of these tasks (the shape and
-// alignment it needs, at least 1024 workgroups, the kernel enabled), and its launch.
+// alignment it needs, at least one workgroup per CU (256), the kernel enabled), and its launch.
 bool panel16_takes(const GemmTask& one, int ntasks);
 int panel16_launch(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one);
 

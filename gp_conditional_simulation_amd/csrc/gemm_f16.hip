@@ -3,8 +3,11 @@
 
 namespace gpex {
 
+// At least one 256 x 256 workgroup per CU: from there the row-panel kernel beat the 128 x 128 /
+// 128 x 256 kernels at every measured shape (N = 16,384, 2,048 columns: 512 workgroups, 1.41 ->
+// 0.90 ms; N = 40,000 at tile 512, 1,000 columns: 632 workgroups, 2.68 -> 2.03 ms).
 bool panel16_takes(const GemmTask& one, int ntasks) {
-    return g_panel16 && ntasks > 0 && panel16_fits(one) && (int64_t)ntasks * (one.M / P16_BM) * (one.N / P16_BN) >= 1024;
+    return g_panel16 && ntasks > 0 && panel16_fits(one) && (int64_t)ntasks * (one.M / P16_BM) * (one.N / P16_BN) >= 256;
 }
 
 int panel16_launch(gpex_ctx_t ctx, hipStream_t s, const GemmTask* d_tasks, int ntasks, const GemmTask& one) {

@@ -597,7 +597,7 @@ static int try_typed(hipStream_t s, const GemmTask* d_tasks, int ntasks, const G
     if constexpr (sizeof(CT) == 2 && ROLE == GEMM_TRMM && TRA == 1 && TRB == 0 && std::is_same<TA, _Float16>::value &&
                   std::is_same<TB, _Float16>::value && std::is_same<TC, double>::value) {
         // row panels of the simulation product: 256 x 256 blocks (panel16.h) when the part is all
-        // of C and that still leaves at least 1024 workgroups
+        // of C and that still leaves at least one workgroup per CU
         const bool whole = p.fast && p.m_off == 0 && p.n_off == 0 && p.bmc * BM == one.M && p.bnc * BN == one.N;
         if (whole && panel16_takes(one, ntasks)) {
             const Part w{0, 0, one.M / P16_BM, one.N / P16_BN, true};
