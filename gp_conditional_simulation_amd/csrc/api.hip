@@ -103,6 +103,16 @@ int ctx_event(gpex_ctx_t ctx, size_t i, hipEvent_t* out) {
     return GPEX_OK;
 }
 
+int ctx_timing_event(gpex_ctx_t ctx, size_t i, hipEvent_t* out) {
+    while (ctx->tevents.size() <= i) {
+        hipEvent_t e;
+        GPEX_HIP(ctx, hipEventCreate(&e));
+        ctx->tevents.push_back(e);
+    }
+    *out = ctx->tevents[i];
+    return GPEX_OK;
+}
+
 }  // namespace gpex
 
 using namespace gpex;
@@ -129,7 +139,8 @@ extern "C" int gpex_ctx_create(int device, void* hip_stream, void* (*alloc)(size
         return GPEX_ERR_NOMEM;
     }
     if (hipMemsetAsync(c->d_flags, 0, sizeof(long long) * FLAG_COUNT, c->stream) != hipSuccess ||
-        hipStreamSynchronize(c->stream) != hipSuccess) {
+        hipStreamSynchronize(c->stream) != hipSuccess ||
+        hipHostMalloc((void**)&c->h_ret, sizeof(long long) * (FLAG_COUNT + 1), hipHostMallocDefault) != hipSuccess) {
         dev_free(c, c->d_flags);
         delete c;
         return GPEX_ERR_HIP;
@@ -167,6 +178,8 @@ extern "C" int gpex_ctx_destroy(gpex_ctx_t ctx) {
     if (ctx->side_fork) (void)hipEventDestroy(ctx->side_fork);
     if (ctx->side_join) (void)hipEventDestroy(ctx->side_join);
     for (auto e : ctx->events) (void)hipEventDestroy(e);
+    for (auto e : ctx->tevents) (void)hipEventDestroy(e);
+    if (ctx->h_ret) (void)hipHostFree(ctx->h_ret);
     delete ctx;
     return GPEX_OK;
 }

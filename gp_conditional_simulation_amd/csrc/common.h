@@ -51,6 +51,11 @@ struct gpex_ctx_s {
     // look-ahead stream of the factorization and its event pool (created on first use, kept)
     hipStream_t ahead = nullptr;
     std::vector<hipEvent_t> events;
+    // timing events of the simulation product's phase timings (created on first use, kept)
+    std::vector<hipEvent_t> tevents;
+    // pinned host words for the simulation product's end-of-call readback (flags, then ||B||^2),
+    // allocated with the context
+    long long* h_ret = nullptr;
 };
 
 struct gpex_tiled_s {
@@ -140,6 +145,8 @@ struct Carve {
 };
 // A timing-disabled event from the context's pool (index i, created on first use).
 int ctx_event(gpex_ctx_t ctx, size_t i, hipEvent_t* out);
+// A timing-enabled event from the context's second pool (index i, created on first use).
+int ctx_timing_event(gpex_ctx_t ctx, size_t i, hipEvent_t* out);
 // Device address of the fixed scratch array of the allocation-free entry points on `device`
 // (NULL before a context was created on it).
 constexpr size_t SCRATCH_BYTES = size_t(32) << 20;

@@ -15,6 +15,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include <cstring>
 #include "common.h"
 #include "devutil.h"
 
@@ -483,7 +484,7 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     GPEX_HIP(ctx, hipMemsetAsync(ctx->d_flags + FLAG_FP16_OVF, 0, sizeof(long long) * (FLAG_BADTASK - FLAG_FP16_OVF + 1), s));
     hipEvent_t ev[6] = {};
     if (ctx->timing) {
-        for (auto& e : ev) (void)hipEventCreate(&e);
+        for (size_t q = 0; q < 6; ++q) GPEX_TRY(ctx_timing_event(ctx, q, &ev[q]));
         (void)hipEventRecord(ev[0], s);
     }
     hipLaunchKernelGGL(k_make_B, dim3((unsigned)nblkB), dim3(256), 0, s, d_Z, n, nsim, seed, rows,
@@ -508,14 +509,20 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         (void)hipEventRecord(ev[2], s);
         (void)hipEventRecord(ev[3], s);
     }
-    // ||Z / s||_F^2: the block partials folded on the device in a fixed order, one value back
+    // ||Z / s||_F^2: the block partials folded on the device in a fixed order, one value back;
+    // both readbacks land in the context's pinned words
     double ss = 0.0;
     long long flags[FLAG_COUNT] = {};
     if (diag) hipLaunchKernelGGL(k_fold_sum, dim3(1), dim3(FOLD_THR), 0, s, part, nblkB, part + nblkB);
     hipError_t e = hipGetLastError();
-    if (e == hipSuccess && diag) e = hipMemcpyAsync(&ss, part + nblkB, sizeof(double), hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipMemcpyAsync(flags, ctx->d_flags, sizeof(flags), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && diag)
+        e = hipMemcpyAsync(ctx->h_ret + FLAG_COUNT, part + nblkB, sizeof(double), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(ctx->h_ret, ctx->d_flags, sizeof(flags), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);   // also keeps `tasks` alive for its upload
+    if (e == hipSuccess) {
+        std::memcpy(flags, ctx->h_ret, sizeof(flags));
+        if (diag) std::memcpy(&ss, ctx->h_ret + FLAG_COUNT, sizeof(double));
+    }
     if (r < 0) return r;
     if (e != hipSuccess) return set_err(ctx, GPEX_ERR_HIP, std::string("trmm sync: ") + hipGetErrorString(e));
     if (ctx->timing) {
@@ -527,7 +534,6 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
         ctx->timings[11] = b;
         ctx->timings[18] = c;
         ctx->timings[19] = whole_rows ? 1.0 : 0.0;
-        for (auto& e2 : ev) (void)hipEventDestroy(e2);
     }
     if (diag) {
         *diag = L->diag;
