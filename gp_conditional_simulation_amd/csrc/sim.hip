@@ -398,6 +398,19 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     auto* fl = reinterpret_cast<unsigned long long*>(ctx->d_flags);
     const int32_t kround = emu ? (int32_t)nb : 0;
 
+    // B first: the normals run on the device while the host builds and uploads the task list
+    GPEX_HIP(ctx, hipMemsetAsync(ctx->d_flags + FLAG_FP16_OVF, 0, sizeof(long long) * (FLAG_BADTASK - FLAG_FP16_OVF + 1), s));
+    hipEvent_t ev[6] = {};
+    if (ctx->timing) {
+        for (size_t q = 0; q < 6; ++q) GPEX_TRY(ctx_timing_event(ctx, q, &ev[q]));
+        (void)hipEventRecord(ev[0], s);
+    }
+    hipLaunchKernelGGL(k_make_B, dim3((unsigned)nblkB), dim3(256), 0, s, d_Z, n, nsim, seed, rows,
+                       1.0 / L->s, amp, B, part, fl);
+    if (npad > 0)
+        hipLaunchKernelGGL(k_zero_pad, dim3((unsigned)((npad + 255) / 256)), dim3(256), 0, s, n, nsim, rows, cols, amp, B);
+    GPEX_HIP(ctx, hipGetLastError());
+
     std::vector<GemmTask> tasks;   // uploaded once; alive until the final synchronisation
     // diagonal tiles: FP32 products of cast32(L_kk) and cast32(B_k) (mixed precision) or FP64
     auto diag_task = [&](int64_t k, double beta) {
@@ -481,17 +494,6 @@ extern "C" int gpex_trmm_sim(gpex_ctx_t ctx, gpex_tiled_t L, int64_t nsim, uint6
     }
     if (tasks.size() > ntask) return set_err(ctx, GPEX_ERR_STATE, "gpex_trmm_sim: task count exceeds its workspace");
     GPEX_HIP(ctx, hipMemcpyAsync(d_tasks, tasks.data(), sizeof(GemmTask) * tasks.size(), hipMemcpyHostToDevice, s));
-    GPEX_HIP(ctx, hipMemsetAsync(ctx->d_flags + FLAG_FP16_OVF, 0, sizeof(long long) * (FLAG_BADTASK - FLAG_FP16_OVF + 1), s));
-    hipEvent_t ev[6] = {};
-    if (ctx->timing) {
-        for (size_t q = 0; q < 6; ++q) GPEX_TRY(ctx_timing_event(ctx, q, &ev[q]));
-        (void)hipEventRecord(ev[0], s);
-    }
-    hipLaunchKernelGGL(k_make_B, dim3((unsigned)nblkB), dim3(256), 0, s, d_Z, n, nsim, seed, rows,
-                       1.0 / L->s, amp, B, part, fl);
-    if (npad > 0)
-        hipLaunchKernelGGL(k_zero_pad, dim3((unsigned)((npad + 255) / 256)), dim3(256), 0, s, n, nsim, rows, cols, amp, B);
-    GPEX_HIP(ctx, hipGetLastError());
     if (ctx->timing) (void)hipEventRecord(ev[1], s);
     int r = GPEX_OK;
     // the row panels' launch (timed on its own): the last one of the fused product
